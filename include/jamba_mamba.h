@@ -1,0 +1,191 @@
+/*
+ * jamba_mamba.h -- C ABI of the MI355X (gfx950) Mamba mixer layer library.
+ *
+ * The layer is the Mamba (selective state-space) block that fills seven of every
+ * eight layers of Jamba (Jamba: A Hybrid Transformer-Mamba Language Model, §2
+ * "Model architecture" and §3.1: blocks of l=8 layers with attention:Mamba =
+ * 1:7). It carries no positional input (same paper, §6.5) and keeps a fixed-size
+ * state per sequence in place of a KV cache (§2, the KV-cache paragraph and
+ * Table 1), which is what the decode entry point carries between tokens.
+ *
+ * Per token t of a sequence (the pages give no formulas; this is the standard
+ * selective-SSM block of the paper's citation [17]):
+ *   [x ; z]        = W_in u_t                      in_proj   (x rows first)
+ *   x^_t           = SiLU(b_conv + sum_k w_conv[:,k] * x_{t-3+k})   causal depthwise conv, k=4
+ *   [delta; B; C]  = W_x x^_t                      x_proj    (rows delta | B | C)
+ *   Delta_t        = softplus(W_dt delta + b_dt)   dt_proj
+ *   h_t            = exp(Delta_t A) h_{t-1} + Delta_t B_t x^_t,  A = -exp(A_log)
+ *   y_t            = C_t . h_t + D x^_t
+ *   out_t          = W_out (y_t * SiLU(z_t))       gate + out_proj
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the name ends in _host. All tensors are
+ *    dense row-major, owned by the caller, and must stay valid until the work
+ *    enqueued on `stream` has finished. Weights are only read.
+ *  - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work and
+ *    return without synchronising the host.
+ *  - Every argument is validated on the host before anything is enqueued; on an
+ *    error nothing is enqueued and a jm_status other than JM_OK is returned, with
+ *    a detail message from jm_last_error() (thread-local). Launch failures return
+ *    JM_ERR_HIP; faults inside kernels surface at the caller's next synchronisation.
+ *  - The library never allocates device memory in these calls: temporaries live in
+ *    the caller's workspace, sized by the *_workspace_size queries.
+ *  - Calls on different streams with different workspaces may run concurrently.
+ *  - Supported shapes: d_state == 16, d_conv == 4, d_model, d_inner % 64 == 0,
+ *    dt_rank % 8 == 0; act/weight dtypes either both JM_F32 or both JM_BF16.
+ *    A_log, D and dt_proj_b are fp32 and the SSM state is fp32 in both cases.
+ */
+#ifndef JAMBA_MAMBA_H
+#define JAMBA_MAMBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JM_OK = 0,
+    JM_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad enum value          */
+    JM_ERR_SHAPE = 2,         /* cu_seqlens / token count / batch inconsistent         */
+    JM_ERR_UNSUPPORTED = 3,   /* a dimension or dtype combination the kernels lack     */
+    JM_ERR_ALIGNMENT = 4,     /* a pointer not 16-byte aligned                         */
+    JM_ERR_WORKSPACE = 5,     /* workspace null or smaller than the query returned     */
+    JM_ERR_HIP = 6            /* a HIP runtime call failed (message in jm_last_error)  */
+} jm_status;
+
+typedef enum { JM_F32 = 0, JM_BF16 = 1 } jm_dtype;
+
+/* Layer sizes and dtypes (the sizes the Jamba-7B-class Mamba layer uses are
+ * d_model 4096, d_inner 8192, d_state 16, d_conv 4, dt_rank 256). */
+typedef struct {
+    int32_t d_model;
+    int32_t d_inner;
+    int32_t d_state;
+    int32_t d_conv;
+    int32_t dt_rank;
+    int32_t act_dtype;     /* jm_dtype of u, out, conv state and activations      */
+    int32_t weight_dtype;  /* jm_dtype of in/x/dt/out projections and conv weights */
+} jm_layer_dims;
+
+/* Layer parameters; element type `weight_dtype` unless marked fp32. */
+typedef struct {
+    const void  *in_proj_w;   /* (2*d_inner, d_model): rows [0, d_inner) give x, the rest z */
+    const void  *conv_w;      /* (d_inner, d_conv): tap d_conv-1 multiplies the current token */
+    const void  *conv_b;      /* (d_inner) or NULL for no bias                                */
+    const void  *x_proj_w;    /* (dt_rank + 2*d_state, d_inner): rows delta | B | C            */
+    const void  *dt_proj_w;   /* (d_inner, dt_rank)                                            */
+    const float *dt_proj_b;   /* (d_inner) fp32                                                */
+    const float *A_log;       /* (d_inner, d_state) fp32; A = -exp(A_log)                      */
+    const float *D;           /* (d_inner) fp32 skip weight                                    */
+    const void  *out_proj_w;  /* (d_model, d_inner)                                            */
+} jm_layer_weights;
+
+/* Human-readable name of a status. Never NULL. */
+const char *jm_status_string(jm_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *jm_last_error(void);
+
+/* Bytes of device workspace jamba_mamba_prefill needs for this many packed tokens
+ * and sequences. */
+jm_status jm_prefill_workspace_size(const jm_layer_dims *dims, int32_t n_seqs,
+                                    int64_t total_tokens, size_t *bytes);
+
+/* Bytes of device workspace jamba_mamba_decode_step needs for `batch` sequences. */
+jm_status jm_decode_workspace_size(const jm_layer_dims *dims, int32_t batch, size_t *bytes);
+
+/*
+ * Prefill over packed variable-length sequences (the long-context path: one
+ * sequence of 128K tokens runs in parallel along its length through a chunked
+ * scan). Sequence i is rows cu_seqlens[i] .. cu_seqlens[i+1]-1 of u/out; every
+ * sequence starts from its own initial state (or zeros) and never sees another.
+ *
+ *  u                (total_tokens, d_model)  act_dtype, read
+ *  cu_seqlens       (n_seqs + 1) int32 on the device, read by the kernels
+ *  cu_seqlens_host  the same values in host memory (validation and planning);
+ *                   must equal the device copy. cu[0] == 0, strictly increasing
+ *                   (empty sequences are rejected), cu[n_seqs] == total_tokens.
+ *  init_conv_state  (n_seqs, d_inner, d_conv-1) act_dtype or NULL (zeros): the
+ *                   d_conv-1 pre-conv x values before each sequence, oldest first
+ *  init_ssm_state   (n_seqs, d_inner, d_state) fp32 or NULL (zeros)
+ *  out              (total_tokens, d_model) act_dtype, written
+ *  final_conv_state (n_seqs, d_inner, d_conv-1) act_dtype or NULL: the last
+ *                   d_conv-1 pre-conv x values of each sequence, oldest first
+ *                   (may be the same buffer as init_conv_state)
+ *  final_ssm_state  (n_seqs, d_inner, d_state) fp32 or NULL: h after each
+ *                   sequence's last token (must NOT overlap init_ssm_state)
+ *  workspace        >= jm_prefill_workspace_size bytes, 256-byte aligned
+ * total_tokens must be below 2^31.
+ */
+jm_status jamba_mamba_prefill(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                              const void *u, const int32_t *cu_seqlens,
+                              const int32_t *cu_seqlens_host, int32_t n_seqs,
+                              int64_t total_tokens,
+                              const void *init_conv_state, const float *init_ssm_state,
+                              void *out, void *final_conv_state, float *final_ssm_state,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: one new token for each of `batch` sequences, updating the
+ * carried state in place (the constant-size replacement of a KV cache).
+ *
+ *  u           (batch, d_model) act_dtype, read
+ *  conv_state  (batch, d_inner, d_conv-1) act_dtype, read and overwritten with the
+ *              shifted window (oldest first)
+ *  ssm_state   (batch, d_inner, d_state) fp32, read and overwritten
+ *  out         (batch, d_model) act_dtype, written
+ *  workspace   >= jm_decode_workspace_size bytes, 256-byte aligned
+ */
+jm_status jamba_mamba_decode_step(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                                  const void *u, int32_t batch, void *conv_state,
+                                  float *ssm_state, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* ---- Plan inspection (host only; for tests of the packed-sequence indexing) ---- */
+
+/* One run of consecutive tokens inside one scan chunk that belong to one sequence. */
+typedef struct {
+    int32_t chunk;        /* chunk index                                   */
+    int32_t seq;          /* sequence index                                */
+    int32_t begin;        /* first packed token row of the run             */
+    int32_t end;          /* one past the last row                         */
+    int32_t starts_seq;   /* 1 if `begin` is the sequence's first token    */
+    int32_t ends_seq;     /* 1 if `end - 1` is the sequence's last token   */
+} jm_chunk_segment;
+
+/*
+ * The chunking jamba_mamba_prefill uses for these sequences: chunk c covers rows
+ * [c*chunk_len, min((c+1)*chunk_len, total_tokens)). Writes *chunk_len and
+ * *n_chunks, and up to max_segments segments in chunk order (then row order);
+ * *n_segments receives the full count. `segments` may be NULL when max_segments is 0.
+ */
+jm_status jm_prefill_plan(const jm_layer_dims *dims, const int32_t *cu_seqlens_host,
+                          int32_t n_seqs, int64_t total_tokens, int32_t *chunk_len,
+                          int32_t *n_chunks, jm_chunk_segment *segments,
+                          int64_t max_segments, int64_t *n_segments);
+
+/* Chunk length override for the scan (0 = automatic). Process-wide; for tuning
+ * and for chunk-count invariance tests. Returns JM_ERR_INVALID_ARG if negative. */
+jm_status jm_set_scan_chunk_len(int32_t chunk_len);
+
+/* ---- Kernel timing (diagnostics; the benchmark reads per-kernel durations) ----
+ * While enabled, every kernel the library enqueues is bracketed by a pair of HIP
+ * events on the caller's stream. jm_profile_read synchronises those events and
+ * reports, per kernel name, the number of launches and the summed milliseconds
+ * since the last reset. Not for concurrent use from several threads. */
+jm_status jm_profile_enable(int32_t enable);
+jm_status jm_profile_reset(void);
+typedef struct {
+    char    name[32];
+    int64_t launches;
+    double  total_ms;
+} jm_kernel_time;
+jm_status jm_profile_read(jm_kernel_time *out, int32_t max_entries, int32_t *n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JAMBA_MAMBA_H */

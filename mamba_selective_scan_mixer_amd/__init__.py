@@ -1,0 +1,291 @@
+"""Python binding of the MI355X Mamba mixer layer library (libjamba_mamba.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory and the stream; the functions here check
+device, dtype, shape and contiguity of torch tensors, then pass raw pointers to
+the C ABI declared in include/jamba_mamba.h (same names). There is no fallback:
+if the library is not built, importing `lib()` raises.
+
+The layer (Jamba: A Hybrid Transformer-Mamba Language Model, §2 "Model
+architecture" -- the Mamba layers that make up 7 of every 8 Jamba layers):
+in_proj -> causal conv1d(k=4) + SiLU -> x_proj -> softplus(dt_proj) -> selective
+scan -> D skip and SiLU(z) gate -> out_proj, with a fixed-size conv/SSM state per
+sequence in place of a KV cache.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libjamba_mamba.so")
+
+JM_F32 = 0
+JM_BF16 = 1
+_STATUS = ["JM_OK", "JM_ERR_INVALID_ARG", "JM_ERR_SHAPE", "JM_ERR_UNSUPPORTED",
+           "JM_ERR_ALIGNMENT", "JM_ERR_WORKSPACE", "JM_ERR_HIP"]
+
+
+class LayerDims(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_inner", ctypes.c_int32),
+                ("d_state", ctypes.c_int32), ("d_conv", ctypes.c_int32),
+                ("dt_rank", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("weight_dtype", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D",
+        "out_proj_w")]
+
+
+class ChunkSegment(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("chunk", "seq", "begin", "end", "starts_seq",
+                                               "ends_seq")]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
+
+
+class JMError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        name = _STATUS[status] if 0 <= status < len(_STATUS) else str(status)
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.status_name = name
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib() -> ctypes.CDLL:
+    """Load libjamba_mamba.so (after torch, so both use the HIP runtime torch loaded)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m mamba_selective_scan_mixer_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.jm_status_string.restype = ctypes.c_char_p
+        L.jm_status_string.argtypes = [ctypes.c_int]
+        L.jm_last_error.restype = ctypes.c_char_p
+        L.jm_last_error.argtypes = []
+        L.jm_prefill_workspace_size.argtypes = [ctypes.POINTER(LayerDims), ctypes.c_int32,
+                                                ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+        L.jm_decode_workspace_size.argtypes = [ctypes.POINTER(LayerDims), ctypes.c_int32,
+                                               ctypes.POINTER(ctypes.c_size_t)]
+        L.jamba_mamba_prefill.argtypes = [
+            ctypes.POINTER(LayerDims), ctypes.POINTER(LayerWeights), _P, _P, _P, ctypes.c_int32,
+            ctypes.c_int64, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.jamba_mamba_decode_step.argtypes = [
+            ctypes.POINTER(LayerDims), ctypes.POINTER(LayerWeights), _P, ctypes.c_int32, _P, _P,
+            _P, _P, ctypes.c_size_t, _P]
+        L.jm_prefill_plan.argtypes = [
+            ctypes.POINTER(LayerDims), _P, ctypes.c_int32, ctypes.c_int64,
+            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+            ctypes.POINTER(ChunkSegment), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+        L.jm_set_scan_chunk_len.argtypes = [ctypes.c_int32]
+        L.jm_profile_enable.argtypes = [ctypes.c_int32]
+        L.jm_profile_reset.argtypes = []
+        L.jm_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32)]
+        for name in ("jm_prefill_workspace_size", "jm_decode_workspace_size", "jamba_mamba_prefill",
+                     "jamba_mamba_decode_step", "jm_prefill_plan", "jm_set_scan_chunk_len",
+                     "jm_profile_enable", "jm_profile_reset", "jm_profile_read"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise JMError(status, lib().jm_last_error().decode())
+
+
+def make_dims(d_model: int, d_inner: int, d_state: int = 16, d_conv: int = 4,
+              dt_rank: int = 8, dtype: torch.dtype = torch.bfloat16) -> LayerDims:
+    code = {torch.bfloat16: JM_BF16, torch.float32: JM_F32}[dtype]
+    return LayerDims(d_model, d_inner, d_state, d_conv, dt_rank, code, code)
+
+
+def _torch_dtype(dims: LayerDims) -> torch.dtype:
+    return torch.bfloat16 if dims.act_dtype == JM_BF16 else torch.float32
+
+
+class MambaLayer:
+    """Device-resident parameters of one layer plus the C structs that point at them."""
+
+    WEIGHT_KEYS = ("in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b",
+                   "A_log", "D", "out_proj_w")
+    FP32_KEYS = ("dt_proj_b", "A_log", "D")
+
+    def __init__(self, dims: LayerDims, tensors: Dict[str, torch.Tensor]):
+        self.dims = dims
+        dt = _torch_dtype(dims)
+        di, dm, N, K, R = dims.d_inner, dims.d_model, dims.d_state, dims.d_conv, dims.dt_rank
+        shapes = {"in_proj_w": (2 * di, dm), "conv_w": (di, K), "conv_b": (di,),
+                  "x_proj_w": (R + 2 * N, di), "dt_proj_w": (di, R), "dt_proj_b": (di,),
+                  "A_log": (di, N), "D": (di,), "out_proj_w": (dm, di)}
+        self.tensors: Dict[str, Optional[torch.Tensor]] = {}
+        for k in self.WEIGHT_KEYS:
+            t = tensors.get(k)
+            if t is None:
+                if k == "conv_b":
+                    self.tensors[k] = None
+                    continue
+                raise ValueError(f"missing weight {k}")
+            want = torch.float32 if k in self.FP32_KEYS else dt
+            if t.dtype != want or tuple(t.shape) != shapes[k] or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{k}: need contiguous {want} {shapes[k]} on the GPU, got "
+                                 f"{t.dtype} {tuple(t.shape)} on {t.device}")
+            self.tensors[k] = t
+        self.struct = LayerWeights(*[(self.tensors[k].data_ptr() if self.tensors[k] is not None
+                                      else None) for k in self.WEIGHT_KEYS])
+
+    @classmethod
+    def from_arrays(cls, dims: LayerDims, arrays: Dict[str, "object"], device="cuda") -> "MambaLayer":
+        """Copy host arrays (numpy or torch) to the device in the layer's dtypes."""
+        dt = _torch_dtype(dims)
+        ts = {}
+        for k in cls.WEIGHT_KEYS:
+            if k not in arrays or arrays[k] is None:
+                continue
+            a = torch.as_tensor(arrays[k])
+            ts[k] = a.to(device=device, dtype=torch.float32 if k in cls.FP32_KEYS else dt).contiguous()
+        return cls(dims, ts)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...]):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name}: need contiguous {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)} (contiguous={t.is_contiguous()})")
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def prefill_workspace_size(dims: LayerDims, n_seqs: int, total_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jm_prefill_workspace_size(ctypes.byref(dims), n_seqs, total_tokens,
+                                           ctypes.byref(out)))
+    return out.value
+
+
+def decode_workspace_size(dims: LayerDims, batch: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jm_decode_workspace_size(ctypes.byref(dims), batch, ctypes.byref(out)))
+    return out.value
+
+
+def _host_cu(cu_seqlens_host) -> Tuple[ctypes.Array, int]:
+    vals = [int(v) for v in cu_seqlens_host]
+    return (ctypes.c_int32 * len(vals))(*vals), len(vals) - 1
+
+
+def jamba_mamba_prefill(layer: MambaLayer, u: torch.Tensor, cu_seqlens: torch.Tensor,
+                        cu_seqlens_host: Sequence[int], init_conv_state=None, init_ssm_state=None,
+                        out=None, final_conv_state=None, final_ssm_state=None,
+                        want_final_states: bool = True, workspace=None, stream=None):
+    """Prefill over packed sequences; returns (out, final_conv_state, final_ssm_state)."""
+    d = layer.dims
+    dt = _torch_dtype(d)
+    host, n = _host_cu(cu_seqlens_host)
+    T = host[n] if n > 0 else 0
+    _need(u, "u", dt, (T, d.d_model))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,))
+    K1 = d.d_conv - 1
+    if init_conv_state is not None:
+        _need(init_conv_state, "init_conv_state", dt, (n, d.d_inner, K1))
+    if init_ssm_state is not None:
+        _need(init_ssm_state, "init_ssm_state", torch.float32, (n, d.d_inner, d.d_state))
+    if out is None:
+        out = torch.empty((T, d.d_model), dtype=dt, device=u.device)
+    _need(out, "out", dt, (T, d.d_model))
+    if want_final_states:
+        if final_conv_state is None:
+            final_conv_state = torch.empty((n, d.d_inner, K1), dtype=dt, device=u.device)
+        if final_ssm_state is None:
+            final_ssm_state = torch.empty((n, d.d_inner, d.d_state), dtype=torch.float32,
+                                          device=u.device)
+    if final_conv_state is not None:
+        _need(final_conv_state, "final_conv_state", dt, (n, d.d_inner, K1))
+    if final_ssm_state is not None:
+        _need(final_ssm_state, "final_ssm_state", torch.float32, (n, d.d_inner, d.d_state))
+    need = prefill_workspace_size(d, n, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    _check(lib().jamba_mamba_prefill(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), _ptr(cu_seqlens), host, n, T,
+        _ptr(init_conv_state), _ptr(init_ssm_state), _ptr(out), _ptr(final_conv_state),
+        _ptr(final_ssm_state), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, final_conv_state, final_ssm_state
+
+
+def jamba_mamba_decode_step(layer: MambaLayer, u: torch.Tensor, conv_state: torch.Tensor,
+                            ssm_state: torch.Tensor, out=None, workspace=None, stream=None):
+    """One token per sequence; updates conv_state and ssm_state in place; returns out."""
+    d = layer.dims
+    dt = _torch_dtype(d)
+    b = u.shape[0] if u.dim() == 2 else -1
+    _need(u, "u", dt, (b, d.d_model))
+    _need(conv_state, "conv_state", dt, (b, d.d_inner, d.d_conv - 1))
+    _need(ssm_state, "ssm_state", torch.float32, (b, d.d_inner, d.d_state))
+    if out is None:
+        out = torch.empty((b, d.d_model), dtype=dt, device=u.device)
+    _need(out, "out", dt, (b, d.d_model))
+    need = decode_workspace_size(d, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    _check(lib().jamba_mamba_decode_step(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), b, _ptr(conv_state),
+        _ptr(ssm_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def prefill_plan(dims: LayerDims, cu_seqlens_host: Sequence[int]):
+    """(chunk_len, n_chunks, [segment dicts]) the prefill uses for these sequences."""
+    host, n = _host_cu(cu_seqlens_host)
+    T = host[n] if n > 0 else 0
+    cl, nc, ns = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib().jm_prefill_plan(ctypes.byref(dims), host, n, T, ctypes.byref(cl),
+                                 ctypes.byref(nc), None, 0, ctypes.byref(ns)))
+    segs = (ChunkSegment * max(ns.value, 1))()
+    _check(lib().jm_prefill_plan(ctypes.byref(dims), host, n, T, ctypes.byref(cl),
+                                 ctypes.byref(nc), segs, ns.value, ctypes.byref(ns)))
+    out: List[dict] = [{f: getattr(s, f) for f, _ in ChunkSegment._fields_} for s in segs[:ns.value]]
+    return cl.value, nc.value, out
+
+
+def set_scan_chunk_len(chunk_len: int) -> None:
+    _check(lib().jm_set_scan_chunk_len(chunk_len))
+
+
+def profile_enable(on: bool = True) -> None:
+    _check(lib().jm_profile_enable(1 if on else 0))
+
+
+def profile_reset() -> None:
+    _check(lib().jm_profile_reset())
+
+
+def profile_read() -> Dict[str, Tuple[int, float]]:
+    """{kernel name: (launches, total ms)} since the last reset (synchronises)."""
+    n = ctypes.c_int32(0)
+    _check(lib().jm_profile_read(None, 0, ctypes.byref(n)))
+    arr = (KernelTime * max(n.value, 1))()
+    _check(lib().jm_profile_read(arr, n.value, ctypes.byref(n)))
+    return {a.name.decode(): (a.launches, a.total_ms) for a in arr[:n.value]}

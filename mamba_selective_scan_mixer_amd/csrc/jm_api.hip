@@ -1,0 +1,530 @@
+// C ABI of the Mamba mixer layer library: argument validation, the packed-sequence
+// chunk plan, workspace carving and the launch sequences of prefill and decode.
+// Validation runs entirely on the host before any HIP call, so a rejected call
+// enqueues nothing.
+#include "jamba_mamba.h"
+#include "jm_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+using namespace jm;
+
+namespace {
+
+thread_local std::string g_last_error;
+int32_t g_chunk_override = 0;
+
+jm_status fail(jm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+jm_status ok() {
+  g_last_error.clear();
+  return JM_OK;
+}
+
+// ---- kernel timing -----------------------------------------------------------------
+struct ProfRec {
+  const char* name;
+  hipEvent_t a, b;
+};
+bool g_prof = false;
+std::mutex g_prof_mu;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+int prof_begin(const char* name, hipStream_t s) {
+  if (!g_prof) return -1;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r{name, pool_get(), pool_get()};
+  if (!r.a || !r.b) return -1;
+  (void)hipEventRecord(r.a, s);
+  g_recs.push_back(r);
+  return (int)g_recs.size() - 1;
+}
+
+void prof_end(int idx, hipStream_t s) {
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  (void)hipEventRecord(g_recs[idx].b, s);
+}
+
+#define JM_LAUNCH(name, call)                                                        \
+  do {                                                                               \
+    int prof_idx_ = prof_begin(name, stream);                                        \
+    hipError_t err_ = (call);                                                        \
+    prof_end(prof_idx_, stream);                                                     \
+    if (err_ != hipSuccess)                                                          \
+      return fail(JM_ERR_HIP, "%s launch failed: %s", name, hipGetErrorString(err_)); \
+  } while (0)
+
+// ---- validation ----------------------------------------------------------------------
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t act_size(const jm_layer_dims& d) { return d.act_dtype == JM_BF16 ? 2 : 4; }
+
+jm_status check_dims(const jm_layer_dims* d) {
+  if (!d) return fail(JM_ERR_INVALID_ARG, "dims is NULL");
+  if ((d->act_dtype != JM_F32 && d->act_dtype != JM_BF16) ||
+      (d->weight_dtype != JM_F32 && d->weight_dtype != JM_BF16))
+    return fail(JM_ERR_INVALID_ARG, "unknown dtype (act %d, weight %d)", d->act_dtype,
+                d->weight_dtype);
+  if (d->act_dtype != d->weight_dtype)
+    return fail(JM_ERR_UNSUPPORTED, "act and weight dtypes must match (both fp32 or both bf16)");
+  if (d->d_model <= 0 || d->d_inner <= 0 || d->d_state <= 0 || d->d_conv <= 0 || d->dt_rank <= 0)
+    return fail(JM_ERR_INVALID_ARG, "layer sizes must be positive");
+  if (d->d_state != 16) return fail(JM_ERR_UNSUPPORTED, "d_state must be 16 (got %d)", d->d_state);
+  if (d->d_conv != 4) return fail(JM_ERR_UNSUPPORTED, "d_conv must be 4 (got %d)", d->d_conv);
+  if (d->d_model % 64 || d->d_inner % 64)
+    return fail(JM_ERR_UNSUPPORTED, "d_model and d_inner must be multiples of 64 (got %d, %d)",
+                d->d_model, d->d_inner);
+  if (d->dt_rank % 8)
+    return fail(JM_ERR_UNSUPPORTED, "dt_rank must be a multiple of 8 (got %d)", d->dt_rank);
+  if ((int64_t)d->d_inner * 2 > 0x7fffffff) return fail(JM_ERR_UNSUPPORTED, "d_inner too large");
+  return JM_OK;
+}
+
+jm_status check_weights(const jm_layer_weights* w) {
+  if (!w) return fail(JM_ERR_INVALID_ARG, "weights is NULL");
+  const void* req[] = {w->in_proj_w, w->conv_w, w->x_proj_w, w->dt_proj_w, w->dt_proj_b,
+                       w->A_log, w->D, w->out_proj_w};
+  const char* names[] = {"in_proj_w", "conv_w", "x_proj_w", "dt_proj_w", "dt_proj_b",
+                         "A_log", "D", "out_proj_w"};
+  for (int i = 0; i < 8; ++i) {
+    if (!req[i]) return fail(JM_ERR_INVALID_ARG, "weights->%s is NULL", names[i]);
+    if (!aligned16(req[i])) return fail(JM_ERR_ALIGNMENT, "weights->%s not 16-byte aligned", names[i]);
+  }
+  if (w->conv_b && !aligned16(w->conv_b))
+    return fail(JM_ERR_ALIGNMENT, "weights->conv_b not 16-byte aligned");
+  return JM_OK;
+}
+
+jm_status check_cu(const int32_t* cu, int32_t n_seqs, int64_t total) {
+  if (!cu) return fail(JM_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if (cu[0] != 0) return fail(JM_ERR_SHAPE, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (cu[i + 1] <= cu[i])
+      return fail(JM_ERR_SHAPE, "sequence %d is empty or cu_seqlens decreases (%d -> %d)", i,
+                  cu[i], cu[i + 1]);
+  if ((int64_t)cu[n_seqs] != total)
+    return fail(JM_ERR_SHAPE, "cu_seqlens[n_seqs] = %d but total_tokens = %lld", cu[n_seqs],
+                (long long)total);
+  return JM_OK;
+}
+
+// ---- plan ----------------------------------------------------------------------------
+int scan_block(int d_inner) { return d_inner % 256 == 0 ? 256 : (d_inner % 128 == 0 ? 128 : 64); }
+
+void plan_chunks(const jm_layer_dims& d, int64_t T, int32_t* chunk_len, int32_t* n_chunks) {
+  int64_t cl;
+  if (g_chunk_override > 0) {
+    cl = g_chunk_override;
+  } else {
+    // Aim for ~2048 workgroups (8 per CU) across channel groups x chunks.
+    const int64_t groups = d.d_inner / scan_block(d.d_inner);
+    const int64_t want = (2048 + groups - 1) / groups;
+    cl = (T + want - 1) / want;
+    if (cl < 64) cl = 64;
+    cl = (cl + 15) / 16 * 16;
+  }
+  if (cl > 0x7fffffff) cl = 0x7fffffff;
+  *chunk_len = (int32_t)cl;
+  *n_chunks = (int32_t)((T + cl - 1) / cl);
+}
+
+// ---- workspace layouts -------------------------------------------------------------------
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct PrefillLayout {
+  size_t x, z, xh, delta, Bm, Cm, dt, aggP, aggh, carry, total;
+};
+
+PrefillLayout prefill_layout(const jm_layer_dims& d, int64_t T, int32_t n_chunks) {
+  PrefillLayout L;
+  const size_t a = act_size(d);
+  const size_t di = (size_t)d.d_inner;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.x = take(T * di * a);
+  L.z = take(T * di * a);
+  L.xh = take(T * di * a);
+  L.delta = take(T * (size_t)d.dt_rank * a);
+  L.Bm = take(T * 16 * sizeof(float));
+  L.Cm = take(T * 16 * sizeof(float));
+  L.dt = take(T * di * sizeof(float));
+  const size_t agg = n_chunks > 1 ? (size_t)n_chunks * di * 16 * sizeof(float) : 0;
+  L.aggP = take(agg);
+  L.aggh = take(agg);
+  L.carry = take(agg);
+  L.total = off;
+  return L;
+}
+
+struct DecodeLayout {
+  size_t x, z, xh, delta, Bm, Cm, g, total;
+};
+
+DecodeLayout decode_layout(const jm_layer_dims& d, int64_t b) {
+  DecodeLayout L;
+  const size_t a = act_size(d);
+  const size_t di = (size_t)d.d_inner;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  L.x = take(b * di * a);
+  L.z = take(b * di * a);
+  L.xh = take(b * di * a);
+  L.delta = take(b * (size_t)d.dt_rank * a);
+  L.Bm = take(b * 16 * sizeof(float));
+  L.Cm = take(b * 16 * sizeof(float));
+  L.g = take(b * di * a);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+hipError_t gemm(const T* X, int64_t ldx, const T* W, int64_t ldw, int64_t M, int N, int K,
+                const EpiArgs& e, hipStream_t s) {
+  if constexpr (sizeof(T) == 2)
+    return launch_gemm_bf16(X, ldx, W, ldw, M, N, K, e, s);
+  else
+    return launch_gemm_f32(X, ldx, W, ldw, M, N, K, e, s);
+}
+
+EpiArgs epi_none() {
+  EpiArgs e;
+  std::memset(&e, 0, sizeof(e));
+  return e;
+}
+
+template <typename T>
+jm_status run_prefill(const jm_layer_dims& d, const jm_layer_weights& w, const T* u,
+                      const int32_t* cu, int32_t n_seqs, int64_t n_tok, const T* init_conv,
+                      const float* init_ssm, T* out, T* final_conv, float* final_ssm,
+                      char* ws, int32_t chunk_len, int32_t n_chunks, hipStream_t stream) {
+  const PrefillLayout L = prefill_layout(d, n_tok, n_chunks);
+  T* x = reinterpret_cast<T*>(ws + L.x);
+  T* z = reinterpret_cast<T*>(ws + L.z);
+  T* xh = reinterpret_cast<T*>(ws + L.xh);
+  T* delta = reinterpret_cast<T*>(ws + L.delta);
+  float* Bm = reinterpret_cast<float*>(ws + L.Bm);
+  float* Cm = reinterpret_cast<float*>(ws + L.Cm);
+  float* dt = reinterpret_cast<float*>(ws + L.dt);
+  float* aggP = reinterpret_cast<float*>(ws + L.aggP);
+  float* aggh = reinterpret_cast<float*>(ws + L.aggh);
+  float* carry = reinterpret_cast<float*>(ws + L.carry);
+  T* g = x;  // x is dead once the conv and its final state are done
+  const int di = d.d_inner, dm = d.d_model, R = d.dt_rank;
+  const T* Win = static_cast<const T*>(w.in_proj_w);
+
+  EpiArgs e = epi_none();
+  e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = di;
+  JM_LAUNCH("in_proj", gemm<T>(u, dm, Win, dm, n_tok, 2 * di, dm, e, stream));
+
+  JM_LAUNCH("conv1d_silu",
+            launch_conv_silu<T>(x, xh, static_cast<const T*>(w.conv_w),
+                                static_cast<const T*>(w.conv_b), init_conv, cu, n_seqs, n_tok,
+                                di, stream));
+  if (final_conv)
+    JM_LAUNCH("conv_final", launch_conv_final<T>(x, init_conv, final_conv, cu, n_seqs, di, stream));
+
+  e = epi_none();
+  e.kind = EPI_XPROJ; e.out0 = delta; e.outf0 = Bm; e.outf1 = Cm; e.split = R; e.n_state = 16;
+  JM_LAUNCH("x_proj", gemm<T>(xh, di, static_cast<const T*>(w.x_proj_w), di, n_tok, R + 32, di,
+                              e, stream));
+
+  e = epi_none();
+  e.kind = EPI_SOFTPLUS; e.outf0 = dt; e.bias = w.dt_proj_b;
+  JM_LAUNCH("dt_proj", gemm<T>(delta, R, static_cast<const T*>(w.dt_proj_w), R, n_tok, di, R, e,
+                               stream));
+
+  if (n_chunks > 1) {
+    JM_LAUNCH("scan_chunk_state",
+              launch_scan_chunk_state<T>(xh, dt, w.A_log, Bm, init_ssm, cu, aggP, aggh, n_seqs,
+                                         n_tok, di, chunk_len, n_chunks - 1, stream));
+    JM_LAUNCH("scan_chunk_carry", launch_scan_chunk_carry(aggP, aggh, carry, di, n_chunks, stream));
+  }
+  JM_LAUNCH("scan_chunk_output",
+            launch_scan_chunk_output<T>(xh, dt, w.A_log, Bm, Cm, w.D, z, g, init_ssm, final_ssm,
+                                        n_chunks > 1 ? carry : nullptr, cu, n_seqs, n_tok, di,
+                                        chunk_len, n_chunks, stream));
+
+  e = epi_none();
+  e.kind = EPI_STORE; e.out0 = out; e.ldo = dm;
+  JM_LAUNCH("out_proj", gemm<T>(g, di, static_cast<const T*>(w.out_proj_w), di, n_tok, dm, di, e,
+                                stream));
+  return ok();
+}
+
+template <typename T>
+jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T* u, int32_t b,
+                     T* conv_state, float* ssm_state, T* out, char* ws, hipStream_t stream) {
+  const DecodeLayout L = decode_layout(d, b);
+  T* x = reinterpret_cast<T*>(ws + L.x);
+  T* z = reinterpret_cast<T*>(ws + L.z);
+  T* xh = reinterpret_cast<T*>(ws + L.xh);
+  T* delta = reinterpret_cast<T*>(ws + L.delta);
+  float* Bm = reinterpret_cast<float*>(ws + L.Bm);
+  float* Cm = reinterpret_cast<float*>(ws + L.Cm);
+  T* g = reinterpret_cast<T*>(ws + L.g);
+  const int di = d.d_inner, dm = d.d_model, R = d.dt_rank;
+
+  EpiArgs e = epi_none();
+  e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = di;
+  JM_LAUNCH("dec_in_proj", gemm<T>(u, dm, static_cast<const T*>(w.in_proj_w), dm, b, 2 * di, dm,
+                                   e, stream));
+  JM_LAUNCH("dec_conv", launch_decode_conv<T>(x, xh, conv_state, static_cast<const T*>(w.conv_w),
+                                              static_cast<const T*>(w.conv_b), b, di, stream));
+  e = epi_none();
+  e.kind = EPI_XPROJ; e.out0 = delta; e.outf0 = Bm; e.outf1 = Cm; e.split = R; e.n_state = 16;
+  JM_LAUNCH("dec_x_proj", gemm<T>(xh, di, static_cast<const T*>(w.x_proj_w), di, b, R + 32, di, e,
+                                  stream));
+  JM_LAUNCH("dec_update",
+            launch_decode_update<T>(xh, z, delta, Bm, Cm, static_cast<const T*>(w.dt_proj_w),
+                                    w.dt_proj_b, w.A_log, w.D, ssm_state, g, b, di, R, stream));
+  e = epi_none();
+  e.kind = EPI_STORE; e.out0 = out; e.ldo = dm;
+  JM_LAUNCH("dec_out_proj", gemm<T>(g, di, static_cast<const T*>(w.out_proj_w), di, b, dm, di, e,
+                                    stream));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* jm_status_string(jm_status s) {
+  switch (s) {
+    case JM_OK: return "JM_OK";
+    case JM_ERR_INVALID_ARG: return "JM_ERR_INVALID_ARG";
+    case JM_ERR_SHAPE: return "JM_ERR_SHAPE";
+    case JM_ERR_UNSUPPORTED: return "JM_ERR_UNSUPPORTED";
+    case JM_ERR_ALIGNMENT: return "JM_ERR_ALIGNMENT";
+    case JM_ERR_WORKSPACE: return "JM_ERR_WORKSPACE";
+    case JM_ERR_HIP: return "JM_ERR_HIP";
+  }
+  return "JM_ERR_UNKNOWN";
+}
+
+const char* jm_last_error(void) { return g_last_error.c_str(); }
+
+jm_status jm_set_scan_chunk_len(int32_t chunk_len) {
+  if (chunk_len < 0) return fail(JM_ERR_INVALID_ARG, "chunk_len must be >= 0");
+  g_chunk_override = chunk_len;
+  return ok();
+}
+
+jm_status jm_prefill_workspace_size(const jm_layer_dims* dims, int32_t n_seqs,
+                                    int64_t total_tokens, size_t* bytes) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if (!bytes) return fail(JM_ERR_INVALID_ARG, "bytes is NULL");
+  if (n_seqs < 0 || total_tokens < 0) return fail(JM_ERR_INVALID_ARG, "negative size");
+  if (total_tokens >= ((int64_t)1 << 31)) return fail(JM_ERR_SHAPE, "total_tokens must be < 2^31");
+  if (total_tokens == 0) { *bytes = 0; return ok(); }
+  int32_t cl, nc;
+  plan_chunks(*dims, total_tokens, &cl, &nc);
+  *bytes = prefill_layout(*dims, total_tokens, nc).total;
+  return ok();
+}
+
+jm_status jm_decode_workspace_size(const jm_layer_dims* dims, int32_t batch, size_t* bytes) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if (!bytes) return fail(JM_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 0) return fail(JM_ERR_INVALID_ARG, "negative batch");
+  *bytes = batch == 0 ? 0 : decode_layout(*dims, batch).total;
+  return ok();
+}
+
+jm_status jm_prefill_plan(const jm_layer_dims* dims, const int32_t* cu_host, int32_t n_seqs,
+                          int64_t total_tokens, int32_t* chunk_len, int32_t* n_chunks,
+                          jm_chunk_segment* segments, int64_t max_segments,
+                          int64_t* n_segments) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if (!chunk_len || !n_chunks || !n_segments)
+    return fail(JM_ERR_INVALID_ARG, "chunk_len, n_chunks and n_segments must not be NULL");
+  if (max_segments > 0 && !segments) return fail(JM_ERR_INVALID_ARG, "segments is NULL");
+  if (n_seqs < 1 || total_tokens < 1) return fail(JM_ERR_SHAPE, "need at least one token");
+  if (total_tokens >= ((int64_t)1 << 31)) return fail(JM_ERR_SHAPE, "total_tokens must be < 2^31");
+  st = check_cu(cu_host, n_seqs, total_tokens);
+  if (st != JM_OK) return st;
+  plan_chunks(*dims, total_tokens, chunk_len, n_chunks);
+  int64_t count = 0;
+  int32_t i = 0;
+  for (int32_t c = 0; c < *n_chunks; ++c) {
+    const int64_t t0 = (int64_t)c * *chunk_len;
+    const int64_t t1 = t0 + *chunk_len < total_tokens ? t0 + *chunk_len : total_tokens;
+    while (cu_host[i + 1] <= t0) ++i;
+    int64_t t = t0;
+    int32_t j = i;
+    while (t < t1) {
+      const int64_t e = cu_host[j + 1] < t1 ? cu_host[j + 1] : t1;
+      if (count < max_segments) {
+        jm_chunk_segment& s = segments[count];
+        s.chunk = c;
+        s.seq = j;
+        s.begin = (int32_t)t;
+        s.end = (int32_t)e;
+        s.starts_seq = cu_host[j] == t ? 1 : 0;
+        s.ends_seq = cu_host[j + 1] == e ? 1 : 0;
+      }
+      ++count;
+      t = e;
+      ++j;
+    }
+  }
+  *n_segments = count;
+  return ok();
+}
+
+jm_status jamba_mamba_prefill(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                              const void* u, const int32_t* cu_seqlens,
+                              const int32_t* cu_seqlens_host, int32_t n_seqs,
+                              int64_t total_tokens, const void* init_conv_state,
+                              const float* init_ssm_state, void* out, void* final_conv_state,
+                              float* final_ssm_state, void* workspace, size_t workspace_bytes,
+                              void* stream_ptr) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  st = check_weights(weights);
+  if (st != JM_OK) return st;
+  if (n_seqs < 0 || total_tokens < 0) return fail(JM_ERR_INVALID_ARG, "negative size");
+  if (total_tokens >= ((int64_t)1 << 31)) return fail(JM_ERR_SHAPE, "total_tokens must be < 2^31");
+  if (n_seqs == 0 || total_tokens == 0) {
+    if (n_seqs != 0 || total_tokens != 0)
+      return fail(JM_ERR_SHAPE, "n_seqs = %d with total_tokens = %lld", n_seqs,
+                  (long long)total_tokens);
+    return ok();   // nothing to do
+  }
+  if (!u || !out || !cu_seqlens)
+    return fail(JM_ERR_INVALID_ARG, "u, out and cu_seqlens must not be NULL");
+  st = check_cu(cu_seqlens_host, n_seqs, total_tokens);
+  if (st != JM_OK) return st;
+  const void* ptrs[] = {u, out, init_conv_state, init_ssm_state, final_conv_state,
+                        final_ssm_state, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  if (init_ssm_state && final_ssm_state) {
+    const char* a = reinterpret_cast<const char*>(init_ssm_state);
+    const char* b = reinterpret_cast<const char*>(final_ssm_state);
+    const size_t bytes = (size_t)n_seqs * dims->d_inner * 16 * sizeof(float);
+    if (a < b + bytes && b < a + bytes)
+      return fail(JM_ERR_INVALID_ARG, "init_ssm_state and final_ssm_state must not overlap");
+  }
+  int32_t cl, nc;
+  plan_chunks(*dims, total_tokens, &cl, &nc);
+  const size_t need = prefill_layout(*dims, total_tokens, nc).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  char* ws = static_cast<char*>(workspace);
+  if (dims->act_dtype == JM_BF16)
+    return run_prefill<bf16>(*dims, *weights, static_cast<const bf16*>(u), cu_seqlens, n_seqs,
+                             total_tokens, static_cast<const bf16*>(init_conv_state),
+                             init_ssm_state, static_cast<bf16*>(out),
+                             static_cast<bf16*>(final_conv_state), final_ssm_state, ws, cl, nc, s);
+  return run_prefill<float>(*dims, *weights, static_cast<const float*>(u), cu_seqlens, n_seqs,
+                            total_tokens, static_cast<const float*>(init_conv_state),
+                            init_ssm_state, static_cast<float*>(out),
+                            static_cast<float*>(final_conv_state), final_ssm_state, ws, cl, nc, s);
+}
+
+jm_status jamba_mamba_decode_step(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                                  const void* u, int32_t batch, void* conv_state,
+                                  float* ssm_state, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream_ptr) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  st = check_weights(weights);
+  if (st != JM_OK) return st;
+  if (batch < 0) return fail(JM_ERR_INVALID_ARG, "negative batch");
+  if (batch == 0) return ok();
+  if (!u || !conv_state || !ssm_state || !out)
+    return fail(JM_ERR_INVALID_ARG, "u, conv_state, ssm_state and out must not be NULL");
+  const void* ptrs[] = {u, conv_state, ssm_state, out, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  const size_t need = decode_layout(*dims, batch).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  char* ws = static_cast<char*>(workspace);
+  if (dims->act_dtype == JM_BF16)
+    return run_decode<bf16>(*dims, *weights, static_cast<const bf16*>(u), batch,
+                            static_cast<bf16*>(conv_state), ssm_state, static_cast<bf16*>(out),
+                            ws, s);
+  return run_decode<float>(*dims, *weights, static_cast<const float*>(u), batch,
+                           static_cast<float*>(conv_state), ssm_state, static_cast<float*>(out), ws,
+                           s);
+}
+
+jm_status jm_profile_enable(int32_t enable) {
+  g_prof = enable != 0;
+  return ok();
+}
+
+jm_status jm_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_recs) {
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return ok();
+}
+
+jm_status jm_profile_read(jm_kernel_time* out, int32_t max_entries, int32_t* n_entries) {
+  if (!n_entries || (max_entries > 0 && !out))
+    return fail(JM_ERR_INVALID_ARG, "out and n_entries must not be NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<jm_kernel_time> agg;
+  for (auto& r : g_recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return fail(JM_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return fail(JM_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+    jm_kernel_time* slot = nullptr;
+    for (auto& a : agg)
+      if (std::strncmp(a.name, r.name, sizeof(a.name)) == 0) slot = &a;
+    if (!slot) {
+      jm_kernel_time t;
+      std::memset(&t, 0, sizeof(t));
+      std::strncpy(t.name, r.name, sizeof(t.name) - 1);
+      agg.push_back(t);
+      slot = &agg.back();
+    }
+    slot->launches += 1;
+    slot->total_ms += ms;
+  }
+  *n_entries = (int32_t)agg.size();
+  for (int32_t i = 0; i < (int32_t)agg.size() && i < max_entries; ++i) out[i] = agg[i];
+  return ok();
+}
+
+}  // extern "C"

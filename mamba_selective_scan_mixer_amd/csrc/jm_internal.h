@@ -1,0 +1,100 @@
+// Internal declarations shared by the library's HIP translation units.
+// Device helpers (bf16 conversion, activations) and the host-side launchers
+// each kernel file provides. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace jm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- scalar conversions ------------------------------------------------------
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// gfx950 converts float->bf16 with round-to-nearest-even in hardware.
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// ---- activations (fp32) --------------------------------------------------------
+// exp(v) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float v) { return __builtin_amdgcn_exp2f(v * kLog2e); }
+// SiLU(v) = v * sigmoid(v).
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + fast_exp(-v)); }
+// softplus(v) = ln(1 + e^v) = max(v, 0) + log1p(e^-|v|): no overflow, and
+// log1p keeps full relative precision for the small step sizes (v << 0).
+__device__ __forceinline__ float softplus(float v) {
+  return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+}
+
+// ---- launchers (host) ------------------------------------------------------------
+enum EpiKind : int {
+  EPI_STORE = 0,     // out0[m*ldo + n] = v                      (act dtype)
+  EPI_SPLIT2 = 1,    // n < split: out0[m*split+n], else out1[m*split + n-split]
+  EPI_XPROJ = 2,     // n < split: delta (act) ; then B, C (fp32, width n_state each)
+  EPI_SOFTPLUS = 3,  // outf[m*N + n] = softplus(v + bias[n])   (fp32)
+  EPI_F32 = 4        // outf[m*N + n] = v                          (fp32)
+};
+
+struct EpiArgs {
+  int kind;
+  void* out0;        // act-dtype output (STORE, SPLIT2 first half, XPROJ delta)
+  void* out1;        // act-dtype output (SPLIT2 second half)
+  float* outf0;      // fp32 output (SOFTPLUS, F32, XPROJ B)
+  float* outf1;      // fp32 output (XPROJ C)
+  const float* bias; // SOFTPLUS bias
+  int split;         // SPLIT2 / XPROJ boundary
+  int n_state;       // XPROJ width of B and C
+  int ldo;           // STORE row stride
+};
+
+// Y[m, n] = sum_k X[m, k] * W[n, k]; X (M, K) row stride ldx, W (N, K) row stride ldw.
+hipError_t launch_gemm_bf16(const bf16* X, int64_t ldx, const bf16* W, int64_t ldw,
+                            int64_t M, int N, int K, const EpiArgs& epi, hipStream_t s);
+hipError_t launch_gemm_f32(const float* X, int64_t ldx, const float* W, int64_t ldw,
+                           int64_t M, int N, int K, const EpiArgs& epi, hipStream_t s);
+
+template <typename T>
+hipError_t launch_conv_silu(const T* x, T* xh, const T* conv_w, const T* conv_b,
+                            const T* init_conv, const int32_t* cu, int n_seqs,
+                            int64_t n_tok, int d_inner, hipStream_t s);
+template <typename T>
+hipError_t launch_conv_final(const T* x, const T* init_conv, T* final_conv,
+                             const int32_t* cu, int n_seqs, int d_inner, hipStream_t s);
+
+// Chunked selective scan: phase A (per-chunk end state and decay product),
+// phase B (carry across chunks), phase C (outputs g and final states).
+template <typename T>
+hipError_t launch_scan_chunk_state(const T* x, const float* dt, const float* A_log,
+                                   const float* Bm, const float* init, const int32_t* cu,
+                                   float* agg_P, float* agg_h, int n_seqs, int64_t n_tok,
+                                   int d_inner, int chunk_len, int n_chunks, hipStream_t s);
+hipError_t launch_scan_chunk_carry(const float* agg_P, const float* agg_h, float* carry,
+                                   int d_inner, int n_chunks, hipStream_t s);
+template <typename T>
+hipError_t launch_scan_chunk_output(const T* x, const float* dt, const float* A_log,
+                                    const float* Bm, const float* Cm, const float* D, const T* z,
+                                    T* g, const float* init, float* final_state,
+                                    const float* carry, const int32_t* cu, int n_seqs,
+                                    int64_t n_tok, int d_inner, int chunk_len, int n_chunks,
+                                    hipStream_t s);
+
+// Decode (one token per sequence).
+template <typename T>
+hipError_t launch_decode_conv(const T* x, T* xh, T* conv_state, const T* conv_w,
+                              const T* conv_b, int batch, int d_inner, hipStream_t s);
+template <typename T>
+hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const float* Bm,
+                                const float* Cm, const T* W_dt, const float* b_dt,
+                                const float* A_log, const float* D, float* ssm_state, T* g,
+                                int batch, int d_inner, int dt_rank, hipStream_t s);
+
+}  // namespace jm

@@ -1,0 +1,280 @@
+// Selective scan of the Mamba mixer layer, chunked along the packed token axis.
+//
+// Recurrence per channel d and state n (A = -exp(A_log), fp32 state):
+//   h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x^_t ;  y_t = C_t . h_t + D x^_t
+// followed by the gate g_t = y_t * SiLU(z_t).
+//
+// One lane owns one channel and keeps all 16 states in registers; B_t and C_t are
+// the same for every channel, so they are read as wave-uniform values. The token
+// axis is cut into chunks so that even one 128K-token sequence fills the GPU:
+//   A  chunk_state : each chunk runs its tokens from a zero state and records the
+//                    end state h_loc and P = exp(A * sum(Delta)) (P = 0 when a
+//                    sequence starts inside the chunk: nothing carries across it);
+//   B  chunk_carry : carry_k = P_{k-1} carry_{k-1} + h_loc_{k-1}, per (d, n);
+//   C  chunk_output: each chunk reruns its tokens from carry_k, emits g and writes
+//                    the final state of every sequence that ends in it.
+// Sequence starts inside a chunk reset the state to the sequence's initial state
+// (or zero); exp is evaluated as exp2 with A pre-scaled by log2(e).
+#include "jm_internal.h"
+
+namespace jm {
+namespace {
+
+constexpr int NS = 16;   // d_state
+
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n_seqs, int64_t t) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ void load_a2(const float* __restrict__ A_log, int d, float a2[NS]) {
+#pragma unroll
+  for (int n = 0; n < NS; ++n) a2[n] = -fast_exp(A_log[(int64_t)d * NS + n]) * kLog2e;
+}
+
+__device__ __forceinline__ void load16(const float* __restrict__ p, float v[NS]) {
+#pragma unroll
+  for (int q = 0; q < NS / 4; ++q) {
+    float4 f = reinterpret_cast<const float4*>(p)[q];
+    v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+  }
+}
+
+__device__ __forceinline__ void store16(float* __restrict__ p, const float v[NS]) {
+#pragma unroll
+  for (int q = 0; q < NS / 4; ++q)
+    reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256)
+void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ dt,
+                             const float* __restrict__ A_log, const float* __restrict__ Bm,
+                             const float* __restrict__ init, const int32_t* __restrict__ cu,
+                             float* __restrict__ agg_P, float* __restrict__ agg_h,
+                             int n_seqs, int64_t n_tok, int d_inner, int chunk_len) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int k = blockIdx.y;
+  const int64_t t0 = (int64_t)k * chunk_len;
+  const int64_t t1 = t0 + chunk_len < n_tok ? t0 + chunk_len : n_tok;
+  float a2[NS], h[NS];
+  load_a2(A_log, d, a2);
+#pragma unroll
+  for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+  float dsum = 0.0f;
+  bool reset = false;
+  int i = find_seq(cu, n_seqs, t0);
+  int64_t t = t0;
+  while (t < t1) {
+    const int64_t s_begin = cu[i], s_end = cu[i + 1];
+    if (s_begin == t) {
+      reset = true;
+      dsum = 0.0f;
+      if (init) load16(init + ((int64_t)i * d_inner + d) * NS, h);
+      else
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+    }
+    const int64_t e = s_end < t1 ? s_end : t1;
+    for (; t < e; ++t) {
+      const float dtv = dt[t * d_inner + d];
+      const float dx = dtv * to_f32(x[t * d_inner + d]);
+      const float* b = Bm + t * NS;
+#pragma unroll
+      for (int n = 0; n < NS; ++n)
+        h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * b[n]);
+      dsum += dtv;
+    }
+    ++i;
+  }
+  float P[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) P[n] = reset ? 0.0f : __builtin_amdgcn_exp2f(a2[n] * dsum);
+  const int64_t o = ((int64_t)k * d_inner + d) * NS;
+  store16(agg_P + o, P);
+  store16(agg_h + o, h);
+}
+
+// One thread per (d, n): sequential over chunks (loads coalesced across threads).
+__global__ __launch_bounds__(256)
+void scan_chunk_carry_kernel(const float* __restrict__ agg_P, const float* __restrict__ agg_h,
+                             float* __restrict__ carry, int64_t dn_count, int n_chunks) {
+  const int64_t dn = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (dn >= dn_count) return;
+  // Chunk 0 always begins a sequence, so its carry is never used; the last
+  // chunk's aggregate is never produced.
+  float c = 0.0f;
+  carry[dn] = c;
+  for (int k = 1; k < n_chunks; ++k) {
+    const int64_t prev = (int64_t)(k - 1) * dn_count + dn;
+    c = fmaf(agg_P[prev], c, agg_h[prev]);
+    carry[(int64_t)k * dn_count + dn] = c;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256)
+void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__ dt,
+                              const float* __restrict__ A_log, const float* __restrict__ Bm,
+                              const float* __restrict__ Cm, const float* __restrict__ Dv,
+                              const T* __restrict__ z, T* __restrict__ g,
+                              const float* __restrict__ init, float* __restrict__ final_state,
+                              const float* __restrict__ carry, const int32_t* __restrict__ cu,
+                              int n_seqs, int64_t n_tok, int d_inner, int chunk_len) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int k = blockIdx.y;
+  const int64_t t0 = (int64_t)k * chunk_len;
+  const int64_t t1 = t0 + chunk_len < n_tok ? t0 + chunk_len : n_tok;
+  float a2[NS], h[NS];
+  load_a2(A_log, d, a2);
+  const float Dd = Dv[d];
+  if (carry) load16(carry + ((int64_t)k * d_inner + d) * NS, h);
+  else
+#pragma unroll
+    for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+  int i = find_seq(cu, n_seqs, t0);
+  int64_t t = t0;
+  while (t < t1) {
+    const int64_t s_begin = cu[i], s_end = cu[i + 1];
+    if (s_begin == t) {
+      if (init) load16(init + ((int64_t)i * d_inner + d) * NS, h);
+      else
+#pragma unroll
+        for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+    }
+    const int64_t e = s_end < t1 ? s_end : t1;
+    for (; t < e; ++t) {
+      const int64_t o = t * d_inner + d;
+      const float dtv = dt[o];
+      const float xv = to_f32(x[o]);
+      const float zv = to_f32(z[o]);
+      const float dx = dtv * xv;
+      const float* b = Bm + t * NS;
+      const float* c = Cm + t * NS;
+      float y = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * b[n]);
+        y = fmaf(c[n], h[n], y);
+      }
+      y = fmaf(Dd, xv, y);
+      g[o] = from_f32<T>(y * silu(zv));
+    }
+    if (e == s_end && final_state) store16(final_state + ((int64_t)i * d_inner + d) * NS, h);
+    ++i;
+  }
+}
+
+// Decode: one token per sequence (block row = sequence), fused dt_proj + softplus +
+// state update + D skip + gate. The state is read and written in place.
+template <typename T>
+__global__ __launch_bounds__(256)
+void decode_update_kernel(const T* __restrict__ xh, const T* __restrict__ z,
+                          const T* __restrict__ delta, const float* __restrict__ Bm,
+                          const float* __restrict__ Cm, const T* __restrict__ W_dt,
+                          const float* __restrict__ b_dt, const float* __restrict__ A_log,
+                          const float* __restrict__ Dv, float* __restrict__ state,
+                          T* __restrict__ g, int d_inner, int dt_rank) {
+  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int bi = blockIdx.y;
+  if (d >= d_inner) return;
+  const T* wrow = W_dt + (int64_t)d * dt_rank;
+  const T* drow = delta + (int64_t)bi * dt_rank;
+  float acc = 0.0f;
+  for (int r = 0; r < dt_rank; ++r) acc = fmaf(to_f32(wrow[r]), to_f32(drow[r]), acc);
+  const float dtv = softplus(acc + b_dt[d]);
+  const int64_t o = (int64_t)bi * d_inner + d;
+  const float xv = to_f32(xh[o]);
+  const float zv = to_f32(z[o]);
+  const float dx = dtv * xv;
+  float a2[NS], h[NS];
+  load_a2(A_log, d, a2);
+  float* st = state + o * NS;
+  load16(st, h);
+  const float* b = Bm + (int64_t)bi * NS;
+  const float* c = Cm + (int64_t)bi * NS;
+  float y = 0.0f;
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * b[n]);
+    y = fmaf(c[n], h[n], y);
+  }
+  store16(st, h);
+  y = fmaf(Dv[d], xv, y);
+  g[o] = from_f32<T>(y * silu(zv));
+}
+
+inline int scan_block(int d_inner) { return d_inner % 256 == 0 ? 256 : (d_inner % 128 == 0 ? 128 : 64); }
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_scan_chunk_state(const T* x, const float* dt, const float* A_log,
+                                   const float* Bm, const float* init, const int32_t* cu,
+                                   float* agg_P, float* agg_h, int n_seqs, int64_t n_tok,
+                                   int d_inner, int chunk_len, int n_chunks, hipStream_t s) {
+  if (n_chunks <= 0) return hipSuccess;
+  const int block = scan_block(d_inner);
+  dim3 grid(d_inner / block, n_chunks);
+  hipLaunchKernelGGL(scan_chunk_state_kernel<T>, grid, dim3(block), 0, s, x, dt, A_log, Bm, init,
+                     cu, agg_P, agg_h, n_seqs, n_tok, d_inner, chunk_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_chunk_carry(const float* agg_P, const float* agg_h, float* carry,
+                                   int d_inner, int n_chunks, hipStream_t s) {
+  const int64_t dn = (int64_t)d_inner * NS;
+  hipLaunchKernelGGL(scan_chunk_carry_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s,
+                     agg_P, agg_h, carry, dn, n_chunks);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scan_chunk_output(const T* x, const float* dt, const float* A_log,
+                                    const float* Bm, const float* Cm, const float* D, const T* z,
+                                    T* g, const float* init, float* final_state,
+                                    const float* carry, const int32_t* cu, int n_seqs,
+                                    int64_t n_tok, int d_inner, int chunk_len, int n_chunks,
+                                    hipStream_t s) {
+  const int block = scan_block(d_inner);
+  dim3 grid(d_inner / block, n_chunks);
+  hipLaunchKernelGGL(scan_chunk_output_kernel<T>, grid, dim3(block), 0, s, x, dt, A_log, Bm, Cm,
+                     D, z, g, init, final_state, carry, cu, n_seqs, n_tok, d_inner, chunk_len);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const float* Bm,
+                                const float* Cm, const T* W_dt, const float* b_dt,
+                                const float* A_log, const float* D, float* ssm_state, T* g,
+                                int batch, int d_inner, int dt_rank, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  dim3 grid((d_inner + 255) / 256, batch);
+  hipLaunchKernelGGL(decode_update_kernel<T>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
+                     b_dt, A_log, D, ssm_state, g, d_inner, dt_rank);
+  return hipGetLastError();
+}
+
+#define JM_INST_SCAN(T)                                                                          \
+  template hipError_t launch_scan_chunk_state<T>(const T*, const float*, const float*,          \
+                                                 const float*, const float*, const int32_t*,    \
+                                                 float*, float*, int, int64_t, int, int, int,   \
+                                                 hipStream_t);                                  \
+  template hipError_t launch_scan_chunk_output<T>(const T*, const float*, const float*,         \
+                                                  const float*, const float*, const float*,     \
+                                                  const T*, T*, const float*, float*,           \
+                                                  const float*, const int32_t*, int, int64_t,   \
+                                                  int, int, int, hipStream_t);                  \
+  template hipError_t launch_decode_update<T>(const T*, const T*, const T*, const float*,        \
+                                              const float*, const T*, const float*,             \
+                                              const float*, const float*, float*, T*, int, int, \
+                                              int, hipStream_t);
+JM_INST_SCAN(float)
+JM_INST_SCAN(bf16)
+#undef JM_INST_SCAN
+
+}  // namespace jm

@@ -1,0 +1,204 @@
+"""Host-side checks of the C-ABI library: it loads, exports what the header declares,
+validates arguments before touching the GPU, and plans packed sequences exactly.
+No test here launches a kernel (this suite runs without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import mamba_selective_scan_mixer_amd as jm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(jm.LIB_PATH):
+        from mamba_selective_scan_mixer_amd import build
+        build.build()
+    return jm.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"jamba_mamba_prefill", "jamba_mamba_decode_step", "jm_prefill_workspace_size"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", jm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = names - exported
+    assert not missing, f"declared but not exported: {missing}"
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_status_strings(L):
+    for i, n in enumerate(jm._STATUS):
+        assert L.jm_status_string(i).decode() == n
+    assert L.jm_status_string(99).decode() == "JM_ERR_UNKNOWN"
+
+
+JAMBA = dict(d_model=4096, d_inner=8192, d_state=16, d_conv=4, dt_rank=256)
+
+
+def dims(**kw):
+    p = dict(JAMBA)
+    p.update(kw)
+    return jm.LayerDims(p["d_model"], p["d_inner"], p["d_state"], p["d_conv"], p["dt_rank"],
+                        p.get("act", jm.JM_BF16), p.get("wt", jm.JM_BF16))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_state=8), jm.JMError), (dict(d_conv=3), jm.JMError), (dict(d_model=100), jm.JMError),
+    (dict(dt_rank=12), jm.JMError), (dict(act=jm.JM_F32), jm.JMError), (dict(act=7), jm.JMError),
+])
+def test_dims_rejected(kw, status):
+    with pytest.raises(status) as ei:
+        jm.prefill_workspace_size(dims(**kw), 1, 10)
+    assert ei.value.status_name in ("JM_ERR_UNSUPPORTED", "JM_ERR_INVALID_ARG")
+
+
+def test_workspace_sizes():
+    d = dims()
+    T = 4096
+    ws = jm.prefill_workspace_size(d, 1, T)
+    # x, z, x^ (bf16) + delta (bf16) + B, C (fp32) + Delta (fp32) at least
+    assert ws >= T * (3 * 8192 * 2 + 256 * 2 + 2 * 16 * 4 + 8192 * 4)
+    assert jm.prefill_workspace_size(d, 0, 0) == 0
+    assert jm.decode_workspace_size(d, 64) >= 64 * 8192 * 2 * 4
+    assert jm.decode_workspace_size(d, 0) == 0
+    big = jm.prefill_workspace_size(d, 1, 131072)
+    assert big > 8 * 2**30   # > 4 GiB tensors at 128K tokens are carved correctly (64-bit sizes)
+    with pytest.raises(jm.JMError):
+        jm.prefill_workspace_size(d, 1, 2**31)
+
+
+class _Fake:
+    """Distinct, 16-byte aligned fake device addresses; never dereferenced (validation fails first)."""
+    def __init__(self):
+        self.next = 0x10000000
+
+    def __call__(self):
+        self.next += 0x100000
+        return self.next
+
+
+def _weights(fake, **override):
+    w = jm.LayerWeights(*[fake() for _ in jm.MambaLayer.WEIGHT_KEYS])
+    for k, v in override.items():
+        setattr(w, k, v)
+    return w
+
+
+def _prefill(L, d, w, cu, T=None, u=1, out=1, ws_bytes=None, ws=1, fake=None, **kw):
+    fake = fake or _Fake()
+    host = (ctypes.c_int32 * len(cu))(*cu)
+    n = len(cu) - 1
+    T = cu[-1] if T is None else T
+    args = dict(u=fake() if u else None, cu=fake(), init_conv=None, init_ssm=None,
+                out=fake() if out else None, fconv=None, fssm=None, ws=fake() if ws else None)
+    args.update(kw)
+    if ws_bytes is None:
+        ws_bytes = jm.prefill_workspace_size(d, n, T) if T > 0 else 0
+    return L.jamba_mamba_prefill(ctypes.byref(d), ctypes.byref(w), args["u"], args["cu"], host, n,
+                                 T, args["init_conv"], args["init_ssm"], args["out"],
+                                 args["fconv"], args["fssm"], args["ws"], ws_bytes, None)
+
+
+def test_prefill_validation_paths(L):
+    f = _Fake()
+    d = dims()
+    w = _weights(f)
+    S = {n: i for i, n in enumerate(jm._STATUS)}
+    assert _prefill(L, d, w, [0, 5, 4], fake=f) == S["JM_ERR_SHAPE"]          # decreasing
+    assert _prefill(L, d, w, [0, 5, 5], fake=f) == S["JM_ERR_SHAPE"]          # empty sequence
+    assert _prefill(L, d, w, [1, 5], T=4, fake=f) == S["JM_ERR_SHAPE"]        # cu[0] != 0
+    assert _prefill(L, d, w, [0, 5], T=6, fake=f) == S["JM_ERR_SHAPE"]        # total mismatch
+    assert _prefill(L, d, w, [0, 5], u=0, fake=f) == S["JM_ERR_INVALID_ARG"]  # null input
+    assert _prefill(L, d, w, [0, 5], ws=0, fake=f) == S["JM_ERR_WORKSPACE"]
+    assert _prefill(L, d, w, [0, 5], ws_bytes=100, fake=f) == S["JM_ERR_WORKSPACE"]
+    assert _prefill(L, d, w, [0, 5], fake=f, init_ssm=0x20000000, fssm=0x20000040) == S["JM_ERR_INVALID_ARG"]
+    assert _prefill(L, d, w, [0, 5], fake=f, out=None) == S["JM_ERR_INVALID_ARG"]
+    wb = _weights(f, A_log=None)
+    assert _prefill(L, d, wb, [0, 5], fake=f) == S["JM_ERR_INVALID_ARG"]
+    assert "A_log" in L.jm_last_error().decode()
+    wa = _weights(f, D=0x30000004)
+    assert _prefill(L, d, wa, [0, 5], fake=f) == S["JM_ERR_ALIGNMENT"]
+    assert _prefill(L, d, w, [0, 5], fake=f, u=1, init_conv=0x40000008) == S["JM_ERR_ALIGNMENT"]
+    # empty input: no sequences, no tokens -> nothing to do
+    assert _prefill(L, d, w, [0], fake=f, u=0, out=0, ws=0) == S["JM_OK"]
+
+
+def test_decode_validation_paths(L):
+    f = _Fake()
+    d = dims()
+    w = _weights(f)
+    S = {n: i for i, n in enumerate(jm._STATUS)}
+    need = jm.decode_workspace_size(d, 4)
+    call = lambda b, u, cs, ss, o, ws, nb: L.jamba_mamba_decode_step(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(w), u, b, cs, ss, o, ws, nb, None)
+    assert call(4, f(), f(), f(), f(), f(), need - 1) == S["JM_ERR_WORKSPACE"]
+    assert call(4, None, f(), f(), f(), f(), need) == S["JM_ERR_INVALID_ARG"]
+    assert call(-1, f(), f(), f(), f(), f(), need) == S["JM_ERR_INVALID_ARG"]
+    assert call(4, f() + 8, f(), f(), f(), f(), need) == S["JM_ERR_ALIGNMENT"]
+    assert call(0, None, None, None, None, None, 0) == S["JM_OK"]
+
+
+def expected_segments(cu, chunk_len):
+    """Independent statement of the chunking: chunk c covers [c*L, min((c+1)*L, T))."""
+    T = cu[-1]
+    segs = []
+    n_chunks = -(-T // chunk_len)
+    for c in range(n_chunks):
+        a, b = c * chunk_len, min((c + 1) * chunk_len, T)
+        for s in range(len(cu) - 1):
+            lo, hi = max(a, cu[s]), min(b, cu[s + 1])
+            if lo < hi:
+                segs.append(dict(chunk=c, seq=s, begin=lo, end=hi, starts_seq=int(lo == cu[s]),
+                                 ends_seq=int(hi == cu[s + 1])))
+    return n_chunks, segs
+
+
+@pytest.mark.parametrize("lengths", [[4096], [131072], [1, 2, 3, 1000, 64, 65, 7],
+                                     [5000] * 16, [1] * 300])
+@pytest.mark.parametrize("chunk_override", [0, 16, 1000])
+def test_plan_matches_independent_chunking(lengths, chunk_override):
+    cu = [0] + list(np.cumsum(lengths))
+    d = dims()
+    jm.set_scan_chunk_len(chunk_override)
+    try:
+        cl, nc, segs = jm.prefill_plan(d, cu)
+    finally:
+        jm.set_scan_chunk_len(0)
+    if chunk_override:
+        assert cl == chunk_override
+    n_exp, segs_exp = expected_segments(cu, cl)
+    assert nc == n_exp
+    assert segs == segs_exp
+    # every token is covered exactly once, every sequence starts and ends exactly once
+    assert sum(s["end"] - s["begin"] for s in segs) == cu[-1]
+    assert sum(s["starts_seq"] for s in segs) == len(lengths)
+    assert sum(s["ends_seq"] for s in segs) == len(lengths)
+
+
+def test_plan_rejects_bad_cu():
+    d = dims()
+    with pytest.raises(jm.JMError):
+        jm.prefill_plan(d, [0, 3, 3])
+    with pytest.raises(jm.JMError):
+        jm.set_scan_chunk_len(-1)

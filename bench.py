@@ -1,0 +1,258 @@
+"""Benchmark: Mamba mixer layer prefill at 128K tokens (and decode at batch 64) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+One step = one jamba_mamba_prefill call over a single 131072-token sequence at the
+Jamba-7B-class layer sizes (d_model 4096, d_inner 8192, d_state 16, d_conv 4,
+dt_rank 256), bf16 activations and weights, fp32 state, inputs resident in HBM.
+Prints ONE JSON line: value = prefill tokens/s of the layer; per-kernel durations
+come from HIP events the library records around each kernel on the call's stream
+during the timed steps. The decode figure (64 sequences, one token per step,
+carried state from a 2048-token prefill each) is reported alongside. The CPU
+oracle is timed on a bounded sample of the same workload as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "Mamba-layer prefill tok/s @128K, decode tok/s @B=64; % HBM/MFMA peak"
+
+
+def kernel_work(T: int, dm: int, di: int, R: int, N: int = 16):
+    """Algorithmic FLOPs and HBM bytes per launch for T tokens (bf16 activations,
+    fp32 Delta/B/C/state): what each kernel must read and write, counted once."""
+    a = 2  # bf16 bytes
+    w = {
+        "in_proj": (2.0 * T * 2 * di * dm, T * dm * a + 2 * di * dm * a + T * 2 * di * a),
+        "conv1d_silu": (8.0 * T * di, T * di * a * 2 + di * 5 * a),
+        "conv_final": (0.0, 3 * di * a * 2),
+        "x_proj": (2.0 * T * (R + 2 * N) * di, T * di * a + (R + 2 * N) * di * a + T * (R * a + 2 * N * 4)),
+        "dt_proj": (2.0 * T * di * R, T * R * a + di * R * a + di * 4 + T * di * 4),
+        "scan_chunk_state": (0.0, T * di * (4 + a) + T * N * 4),
+        "scan_chunk_carry": (0.0, 0.0),   # filled in by the caller (depends on the chunk count)
+        "scan_chunk_output": (0.0, T * di * (4 + a + a + a) + T * 2 * N * 4 + di * N * 4),
+        "out_proj": (2.0 * T * dm * di, T * di * a + dm * di * a + T * dm * a),
+    }
+    return w
+
+
+def bound_of(name: str) -> str:
+    return "mfma" if name in ("in_proj", "out_proj") else "hbm"
+
+
+def make_inputs(seed: int = 0):
+    import synth
+    wl = synth.make_workload("prefill_128k", seed=seed)
+    return wl
+
+
+def cpu_baseline(wl, target_s: float = 15.0):
+    """Time the fp64 oracle on the first tokens of the same sequence (bounded sample)."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    w64 = oracle.as_f64(wl.weights)
+    # calibrate on a small sample, then size the timed sample for ~target_s
+    n0 = 64
+    t = time.perf_counter()
+    oracle.prefill(w64, wl.u[:n0], [0, n0])
+    dt0 = time.perf_counter() - t
+    n = int(min(4096, max(n0, n0 * target_s / max(dt0, 1e-3))))
+    t = time.perf_counter()
+    oracle.prefill(w64, wl.u[:n], [0, n])
+    el = time.perf_counter() - t
+    return {"value": n / el, "unit": "tokens/s", "cores": int(max(blas_threads, omp)),
+            "kind": "oracle",
+            "sample": f"first {n} tokens of the 131072-token sequence, fp64 oracle (numpy matmul "
+                      f"+ C recurrence), {el:.1f} s wall; BLAS threads {blas_threads}, OpenMP {omp}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy first (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this layer's path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_selective_scan_mixer_amd as jm
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    wl = make_inputs()
+    d = wl.dims
+    T = wl.total_tokens
+    dims = jm.make_dims(d.d_model, d.d_inner, d.d_state, d.d_conv, d.dt_rank, torch.bfloat16)
+    layer = jm.MambaLayer.from_arrays(dims, wl.weights)
+    u = torch.as_tensor(wl.u).to(dev, torch.bfloat16)
+    cu = torch.as_tensor(wl.cu_seqlens, dtype=torch.int32).to(dev)
+    out = torch.empty((T, d.d_model), dtype=torch.bfloat16, device=dev)
+    fconv = torch.empty((1, d.d_inner, 3), dtype=torch.bfloat16, device=dev)
+    fssm = torch.empty((1, d.d_inner, 16), dtype=torch.float32, device=dev)
+    ws = torch.empty(jm.prefill_workspace_size(dims, 1, T), dtype=torch.uint8, device=dev)
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s; workspace "
+          f"{ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        a = torch.empty(2**30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    def step():
+        jm.jamba_mamba_prefill(layer, u, cu, wl.cu_seqlens, out=out, final_conv_state=fconv,
+                               final_ssm_state=fssm, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    jm.profile_reset()
+    jm.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    jm.profile_enable(False)
+    prof = jm.profile_read()
+    jm.profile_reset()
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = T * args.steps / elapsed
+    print(f"[bench] prefill {ms_per_step:.2f} ms/step, {value / 1e6:.3f} M tok/s", file=sys.stderr,
+          flush=True)
+
+    cl, nc, _ = jm.prefill_plan(dims, wl.cu_seqlens)
+    work = kernel_work(T, d.d_model, d.d_inner, d.dt_rank)
+    work["scan_chunk_carry"] = (0.0, 3.0 * nc * d.d_inner * 16 * 4)
+    kernels = {}
+    for name, (launches, total_ms) in prof.items():
+        avg = total_ms / max(launches, 1)
+        flops, nbytes = work.get(name, (0.0, 0.0))
+        k = {"launches": launches, "avg_ms": round(avg, 4),
+             "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1) if nbytes else None,
+             "tflops": round(flops / (avg * 1e-3) / 1e12, 1) if flops else None}
+        b = bound_of(name)
+        k["bound"] = b
+        if b == "mfma":
+            k["frac"] = round(k["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+        elif k["gbs"] is not None:
+            k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
+        kernels[name] = k
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"]) if kernels else None
+    roof = None
+    if dom:
+        kd = kernels[dom]
+        if kd["bound"] == "mfma":
+            roof = {"kernel": dom, "bound": "mfma", "achieved": kd["tflops"],
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
+                    "traffic": None}
+        else:
+            roof = {"kernel": dom, "bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": kd["frac"], "traffic": None}
+
+    decode = None
+    if not args.no_decode:
+        decode = run_decode(jm, torch, dev, layer, dims, wl, args.decode_steps)
+        print(f"[bench] decode {decode['us_per_step']:.1f} us/step, "
+              f"{decode['tokens_per_s'] / 1e6:.3f} M tok/s", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl)
+        print(f"[bench] cpu oracle {cpu['value']:.1f} tok/s ({cpu['sample']})", file=sys.stderr,
+              flush=True)
+
+    rec = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_128k: one 131072-token sequence, Mamba layer d_model 4096, "
+                               "d_inner 8192, d_state 16, d_conv 4, dt_rank 256; bf16, fp32 state",
+                   "global_batch": 1, "seq_len": T, "scan_chunk_len": cl, "scan_chunks": nc,
+                   "parallelism": "none (one GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "kernels": kernels,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
+    """Decode at batch 64: states from a 2048-token prefill per sequence (not timed),
+    then `steps` single-token steps, timed back to back."""
+    import synth
+    B, L0 = 64, 2048
+    wl = synth.make_workload("decode_b64", seed=0, steps=steps)
+    d = wl.dims
+    u0 = torch.as_tensor(wl.u).to(dev, torch.bfloat16)
+    cu = torch.as_tensor(wl.cu_seqlens, dtype=torch.int32).to(dev)
+    dec_layer = jm.MambaLayer.from_arrays(dims, wl.weights)
+    _, conv, ssm = jm.jamba_mamba_prefill(dec_layer, u0, cu, wl.cu_seqlens)
+    del u0
+    toks = torch.empty((steps, B, d.d_model), dtype=torch.bfloat16)
+    for s in range(steps):
+        toks[s] = torch.as_tensor(wl.next_decode_tokens()).to(torch.bfloat16)
+    toks = toks.to(dev)
+    out = torch.empty((B, d.d_model), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(jm.decode_workspace_size(dims, B), dtype=torch.uint8, device=dev)
+    for s in range(min(8, steps)):   # warm-up on copies of the state
+        jm.jamba_mamba_decode_step(dec_layer, toks[s], conv.clone(), ssm.clone(), out=out,
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    # per-kernel breakdown in a separate pass (events between kernels perturb short steps)
+    jm.profile_reset()
+    jm.profile_enable(True)
+    for s in range(min(64, steps)):
+        jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    jm.profile_enable(False)
+    prof = jm.profile_read()
+    jm.profile_reset()
+    di, dm, R = d.d_inner, d.d_model, d.dt_rank
+    wbytes = (2 * di * dm + (R + 32) * di + di * R + dm * di) * 2
+    state_bytes = B * di * 16 * 4 * 2 + B * di * 3 * 2 * 2
+    per_step = wbytes + state_bytes + B * dm * 2 * 2
+    return {"batch": B, "context": L0, "steps": steps, "us_per_step": el * 1e6 / steps,
+            "tokens_per_s": B * steps / el,
+            "algorithmic_bytes_per_step": per_step,
+            "hbm_frac": per_step / (el / steps) / 1e9 / HBM_PEAK_GBS,
+            "kernels_us": {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in prof.items()}}
+
+
+if __name__ == "__main__":
+    main()

@@ -2,23 +2,29 @@
 //
 // All four are Y[m, n] = sum_k X[m, k] * W[n, k] with both operands K-contiguous
 // (activations (tokens, K), nn.Linear-style weights (features, K)); they differ
-// only in the epilogue. The bf16 path runs on gfx950 matrix cores
+// only in the epilogue, which is a compile-time parameter (one kernel symbol per
+// projection). The bf16 path runs on gfx950 matrix cores
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation); the fp32 path (small fp32
 // layers) is a plain LDS-tiled FMA kernel.
 //
-// bf16 kernel structure:
-//   * macro tile BM x BN (tokens x features), K step 64, 256 threads = 4 waves;
-//   * operand tiles staged global -> registers -> LDS, double-buffered, with the
-//     next tile's global loads issued before the current tile's MFMAs;
-//   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; chunk c of row r is stored at
-//     chunk position c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive
-//     rows hit 8 different bank groups;
-//   * the MFMA "A" operand is the weight tile and "B" the activation tile, so each
-//     lane ends up owning 4 consecutive output features of one token (8-byte
-//     bf16 stores);
-//   * workgroup -> tile order: consecutive workgroups walk down M inside a group
-//     of GROUP_M row blocks (sharing one weight block), and the 8 XCDs each get a
-//     contiguous range of that order (workgroups are dealt round-robin to XCDs).
+// Main bf16 kernel (K % 32 == 0):
+//   * 256 x 256 macro tile, 512 threads = 8 waves (two per SIMD, so one wave's
+//     waits and address arithmetic overlap the other's MFMAs), wave tile 64 x 128;
+//   * operands go global -> LDS directly (global_load_lds_dwordx4, no VGPR
+//     staging) through a 4-stage ring of 32-deep K slices, so loads run ~2.5
+//     stages ahead of the matrix cores; waits are explicit vmcnt counts;
+//   * LDS rows are 32 bf16 = 4 chunks of 16 bytes; chunk c of row r sits at
+//     c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)), which keeps the 16-byte fragment
+//     reads of 16 consecutive rows on distinct banks (measured: no conflicts);
+//   * the barrier of each stage sits before its last k16 step: the next stage's
+//     first fragments load while the current MFMAs run, and the instruction order
+//     is pinned with sched_group_barrier;
+//   * the MFMA "A" operand is the weight tile and "B" the activation tile, so a
+//     lane owns 4 consecutive output features of one token (8-byte bf16 stores);
+//   * tile order: groups of 4 row blocks share a weight block, and each of the 8
+//     XCDs (workgroups are dealt to them round-robin) gets a contiguous range.
+// Fallback (K % 32 != 0): 128 x 128 tiles staged through registers with zero-
+// filled K tails.
 #include "jm_internal.h"
 
 namespace jm {
@@ -41,13 +47,13 @@ __device__ __forceinline__ void store4(T* p, const float v[4], int valid) {
   }
 }
 
-template <typename T>
+template <typename T, int KIND>
 __device__ __forceinline__ void epilogue(const EpiArgs& e, int64_t m, int n, int N,
                                          float v[4]) {
   int valid = N - n;
   if (valid <= 0) return;
   if (valid > 4) valid = 4;
-  switch (e.kind) {
+  switch (KIND) {
     case EPI_STORE:
       store4<T>(static_cast<T*>(e.out0) + m * e.ldo + n, v, valid);
       break;
@@ -102,9 +108,9 @@ __device__ __forceinline__ void tile_coords(int bid, int n_wg, int tiles_m, int 
 
 constexpr int BK = 64;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
-void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx,
+void gemm_bf16_regstage_kernel(const bf16* __restrict__ X, int64_t ldx,
                       const bf16* __restrict__ W, int64_t ldw,
                       int64_t M, int N, int K, int tiles_m, int tiles_n, EpiArgs epi) {
   constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -223,14 +229,197 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx,
         int n = n0 + wn0 + a * 32 + 8 * q + 4 * khalf;
         float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
                       acc[a][b][4 * q + 3]};
-        epilogue<bf16>(epi, m, n, N, v);
+        epilogue<bf16, EPI>(epi, m, n, N, v);
+      }
+    }
+}
+
+// ---- main bf16 kernel: multi-stage direct-to-LDS ring ----------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Chunk position of 16-byte chunk 0 of row r in a 32-column (64-byte) LDS row.
+__device__ __forceinline__ int swz32(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+template <int CNT>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
+}
+
+constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 4, MS_WN = 2, MS_S = 4, MS_BK = 32;
+constexpr int MS_LDS_BYTES = MS_S * (MS_BM + MS_BN) * MS_BK * 2;
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int S, int BKC, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ W,
+                      int64_t ldw, int64_t M, int N, int K, int tiles_m, int tiles_n,
+                      EpiArgs epi) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int TM = BM / WAVES_M, TN = BN / WAVES_N;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int CPR = BKC / 8;               // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPR;              // rows written by one 1 KB DMA instruction
+  constexpr int XI = BM / RPI / NW;          // DMA instructions per wave per stage (X)
+  constexpr int WI = BN / RPI / NW;          // (W)
+  constexpr int LPS = XI + WI;
+  constexpr int SPS = BKC / 16;              // k16 steps per stage
+  constexpr int STAGE = (BM + BN) * BKC;     // bf16 elements per stage
+  constexpr int NM = FN * FM;                // MFMAs per k16 step
+  constexpr int NR = FN + FM;                // fragment reads per k16 step
+  static_assert(BKC == 32 && SPS == 2 && XI >= 1 && WI >= 1 && S >= 3, "tiling");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  bf16* lds = reinterpret_cast<bf16*>(smem);
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM;
+  const int n0 = tn * BN;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm0 = (wave / WAVES_N) * TM;
+  const int wn0 = (wave % WAVES_N) * TN;
+
+  // Each DMA instruction fills 1 KB of LDS: lane l writes slot l, i.e. row l / CPR,
+  // chunk position l % CPR, so it loads the global chunk that belongs there.
+  // Rows past M / N are clamped to the last row (their results are never stored).
+  const bf16* xsrc[XI];
+  const bf16* wsrc[WI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int row = (wave * XI + i) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz32(row);
+    int64_t grow = m0 + row;
+    if (grow >= M) grow = M - 1;
+    xsrc[i] = X + grow * ldx + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = (wave * WI + i) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ swz32(row);
+    int grow = n0 + row;
+    if (grow >= N) grow = N - 1;
+    wsrc[i] = W + (int64_t)grow * ldw + c * 8;
+  }
+  auto issue = [&](int kt, int buf) {
+    const int k0 = kt * BKC;
+    char* base = reinterpret_cast<char*>(lds + buf * STAGE);
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + k0),
+                                       (lds_void*)(base + (wave * XI + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + k0),
+                                       (lds_void*)(base + BM * BKC * 2 + (wave * WI + i) * 1024),
+                                       16, 0, 0);
+  };
+  const int lrow = lane & 31;
+  const int khalf = lane >> 5;
+  const int sw = swz32(lrow);   // equal for all fragment rows of a lane (they differ by 32s)
+  int offW[FN], offX[FM];
+#pragma unroll
+  for (int a = 0; a < FN; ++a) offW[a] = BM * BKC + (wn0 + a * 32 + lrow) * BKC;
+#pragma unroll
+  for (int b = 0; b < FM; ++b) offX[b] = (wm0 + b * 32 + lrow) * BKC;
+  auto load_frags = [&](int buf, int s, bf16x8* pw, bf16x8* px) {
+    const int c = ((2 * s + khalf) ^ sw) << 3;
+    const bf16* st = lds + buf * STAGE;
+#pragma unroll
+    for (int a = 0; a < FN; ++a) pw[a] = *reinterpret_cast<const bf16x8*>(&st[offW[a] + c]);
+#pragma unroll
+    for (int b = 0; b < FM; ++b) px[b] = *reinterpret_cast<const bf16x8*>(&st[offX[b] + c]);
+  };
+
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int b = 0; b < FM; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+  bf16x8 fw[2][FN], fx[2][FM];
+  auto mfma_range = [&](int cur, int lo, int hi) {
+#pragma unroll
+    for (int i = lo; i < hi; ++i) {
+      const int a = i / FM, b = i % FM;
+      acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][a], fx[cur][b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  const int nk = K / BKC;
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st)
+    if (st < nk) issue(st, st);
+  if (nk >= S - 1) wait_vmcnt<(S - 2) * LPS>(); else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  load_frags(0, 0, fw[0], fx[0]);
+  int rbuf = 0;      // stage being computed
+  int wbuf = S - 1;  // stage the next DMA fills
+  int kt = 0;
+  // Steady state: no conditionals, so the compiler counts outstanding LDS reads exactly.
+  for (; kt + S - 1 < nk; ++kt) {
+    // k16 step 0: fetch step 1's fragments under step 0's MFMAs
+    load_frags(rbuf, 1, fw[1], fx[1]);
+    mfma_range(0, 0, NM);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+    // k16 step 1: half its MFMAs, then the stage barrier, the next DMA and the
+    // next stage's first fragments, interleaved with the other half
+    mfma_range(1, 0, NM / 2);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+    wait_vmcnt<(S - 3) * LPS>();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + S - 1, wbuf);
+    const int nbuf = (rbuf + 1 == S) ? 0 : rbuf + 1;
+    load_frags(nbuf, 0, fw[0], fx[0]);
+    mfma_range(1, NM / 2, NM);
+#pragma unroll
+    for (int q = 0; q < NM / 2; ++q) {
+      if (q < LPS) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 DMA
+      if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    rbuf = nbuf;
+    wbuf = (wbuf + 1 == S) ? 0 : wbuf + 1;
+  }
+  // Drain: the last S-1 stages are already in flight.
+  for (; kt < nk; ++kt) {
+    load_frags(rbuf, 1, fw[1], fx[1]);
+    mfma_range(0, 0, NM);
+    const int nbuf = (rbuf + 1 == S) ? 0 : rbuf + 1;
+    if (kt + 1 < nk) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      load_frags(nbuf, 0, fw[0], fx[0]);
+    }
+    mfma_range(1, 0, NM);
+    rbuf = nbuf;
+  }
+
+  // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
+#pragma unroll
+  for (int a = 0; a < FN; ++a)
+#pragma unroll
+    for (int b = 0; b < FM; ++b) {
+      const int64_t m = m0 + wm0 + b * 32 + lrow;
+      if (m >= M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + a * 32 + 8 * q + 4 * khalf;
+        float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                      acc[a][b][4 * q + 3]};
+        epilogue<bf16, EPI>(epi, m, n, N, v);
       }
     }
 }
 
 // ---- fp32 path ----------------------------------------------------------------------
 // 64x64 tile, 256 threads, each thread 4 tokens x 4 consecutive features.
-template <int BM, int BN, int BKF>
+template <int BM, int BN, int BKF, int EPI>
 __global__ __launch_bounds__(256)
 void gemm_f32_kernel(const float* __restrict__ X, int64_t ldx,
                      const float* __restrict__ W, int64_t ldw,
@@ -267,35 +456,78 @@ void gemm_f32_kernel(const float* __restrict__ X, int64_t ldx,
   }
   for (int i = 0; i < 4; ++i) {
     int64_t m = m0 + ty * 4 + i;
-    if (m < M) epilogue<float>(epi, m, n0 + tx * 4, N, acc[i]);
+    if (m < M) epilogue<float, EPI>(epi, m, n0 + tx * 4, N, acc[i]);
   }
+}
+
+template <int EPI>
+hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ldw, int64_t M,
+                           int N, int K, const EpiArgs& epi, hipStream_t s) {
+  if (K % MS_BK == 0) {
+    const int64_t tiles_m = (M + MS_BM - 1) / MS_BM;
+    const int tiles_n = (N + MS_BN - 1) / MS_BN;
+    const int64_t n_wg = tiles_m * tiles_n;
+    if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+    auto kern = gemm_bf16_kernel<MS_BM, MS_BN, MS_WM, MS_WN, MS_S, MS_BK, EPI>;
+    static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled once
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, MS_LDS_BYTES);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(64 * MS_WM * MS_WN), MS_LDS_BYTES, s, X,
+                       ldx, W, ldw, M, N, K, (int)tiles_m, tiles_n, epi);
+    return hipGetLastError();
+  }
+  constexpr int BM = 128, BN = 128;
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int64_t n_wg = tiles_m * tiles_n;
+  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_bf16_regstage_kernel<BM, BN, 2, 2, EPI>), dim3((unsigned)n_wg),
+                     dim3(256), 0, s, X, ldx, W, ldw, M, N, K, (int)tiles_m, tiles_n, epi);
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_f32_epi(const float* X, int64_t ldx, const float* W, int64_t ldw, int64_t M,
+                          int N, int K, const EpiArgs& epi, hipStream_t s) {
+  constexpr int BM = 64, BN = 64, BKF = 16;
+  const int64_t gy = (M + BM - 1) / BM;
+  if (gy > 65535) return hipErrorInvalidValue;
+  dim3 grid((N + BN - 1) / BN, (unsigned)gy);
+  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BKF, EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw,
+                     M, N, K, epi);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const bf16* X, int64_t ldx, const bf16* W, int64_t ldw,
                             int64_t M, int N, int K, const EpiArgs& epi, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
   if (M <= 0 || N <= 0) return hipSuccess;
-  int64_t tiles_m = (M + BM - 1) / BM;
-  int tiles_n = (N + BN - 1) / BN;
-  int64_t n_wg = tiles_m * tiles_n;
-  if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, 2, 2>), dim3((unsigned)n_wg), dim3(256), 0, s,
-                     X, ldx, W, ldw, M, N, K, (int)tiles_m, tiles_n, epi);
-  return hipGetLastError();
+  switch (epi.kind) {
+    case EPI_STORE: return launch_bf16_epi<EPI_STORE>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_SPLIT2: return launch_bf16_epi<EPI_SPLIT2>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_XPROJ: return launch_bf16_epi<EPI_XPROJ>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_SOFTPLUS: return launch_bf16_epi<EPI_SOFTPLUS>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_F32: return launch_bf16_epi<EPI_F32>(X, ldx, W, ldw, M, N, K, epi, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_f32(const float* X, int64_t ldx, const float* W, int64_t ldw,
                            int64_t M, int N, int K, const EpiArgs& epi, hipStream_t s) {
-  constexpr int BM = 64, BN = 64, BKF = 16;
   if (M <= 0 || N <= 0) return hipSuccess;
-  int64_t gy = (M + BM - 1) / BM;
-  if (gy > 65535 * 16) return hipErrorInvalidValue;
-  dim3 grid((N + BN - 1) / BN, (unsigned)gy);
-  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BKF>), grid, dim3(256), 0, s, X, ldx, W, ldw, M, N,
-                     K, epi);
-  return hipGetLastError();
+  switch (epi.kind) {
+    case EPI_STORE: return launch_f32_epi<EPI_STORE>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_SPLIT2: return launch_f32_epi<EPI_SPLIT2>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_XPROJ: return launch_f32_epi<EPI_XPROJ>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_SOFTPLUS: return launch_f32_epi<EPI_SOFTPLUS>(X, ldx, W, ldw, M, N, K, epi, s);
+    case EPI_F32: return launch_f32_epi<EPI_F32>(X, ldx, W, ldw, M, N, K, epi, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace jm

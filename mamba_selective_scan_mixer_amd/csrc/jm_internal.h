@@ -29,10 +29,19 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 __device__ __forceinline__ float fast_exp(float v) { return __builtin_amdgcn_exp2f(v * kLog2e); }
 // SiLU(v) = v * sigmoid(v).
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + fast_exp(-v)); }
-// softplus(v) = ln(1 + e^v) = max(v, 0) + log1p(e^-|v|): no overflow, and
-// log1p keeps full relative precision for the small step sizes (v << 0).
+// log1p(x) for x in [0, 1] with hardware log2: Kahan's identity
+// log1p(x) = x * ln(u) / (u - 1), u = fl(1 + x), which cancels the rounding of
+// 1 + x and keeps a few-ulp relative error even when x is tiny (u == 1 -> x).
+__device__ __forceinline__ float log1p_unit(float x) {
+  const float u = 1.0f + x;
+  const float d = u - 1.0f;
+  const float l = __builtin_amdgcn_logf(u) * 0.69314718055994531f;
+  return d == 0.0f ? x : x * (l / d);
+}
+// softplus(v) = ln(1 + e^v) = max(v, 0) + log1p(e^-|v|): no overflow, and full
+// relative precision for the small step sizes the layer uses (v << 0).
 __device__ __forceinline__ float softplus(float v) {
-  return fmaxf(v, 0.0f) + log1pf(expf(-fabsf(v)));
+  return fmaxf(v, 0.0f) + log1p_unit(fast_exp(-fabsf(v)));
 }
 
 // ---- launchers (host) ------------------------------------------------------------

@@ -229,12 +229,27 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
         jm.jamba_mamba_decode_step(dec_layer, toks[s], conv.clone(), ssm.clone(), out=out,
                                    workspace=ws)
     torch.cuda.synchronize()
+    # eager: one library call per step from Python
     t0 = time.perf_counter()
     for s in range(steps):
         jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    # per-kernel breakdown in a separate pass (events between kernels perturb short steps)
+    el_eager = time.perf_counter() - t0
+    # graph: G consecutive steps (each with its own tokens) captured once, replayed
+    G = 16
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(G):
+            jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // G)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) * steps / (reps * G)
+    # per-kernel breakdown in a separate eager pass (events between kernels perturb short steps)
     jm.profile_reset()
     jm.profile_enable(True)
     for s in range(min(64, steps)):
@@ -248,7 +263,8 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
     state_bytes = B * di * 16 * 4 * 2 + B * di * 3 * 2 * 2
     per_step = wbytes + state_bytes + B * dm * 2 * 2
     return {"batch": B, "context": L0, "steps": steps, "us_per_step": el * 1e6 / steps,
-            "tokens_per_s": B * steps / el,
+            "tokens_per_s": B * steps / el, "timing": "HIP graph of 16 steps, replayed",
+            "us_per_step_eager": el_eager * 1e6 / steps,
             "algorithmic_bytes_per_step": per_step,
             "hbm_frac": per_step / (el / steps) / 1e9 / HBM_PEAK_GBS,
             "kernels_us": {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in prof.items()}}

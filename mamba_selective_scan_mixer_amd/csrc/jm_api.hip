@@ -183,7 +183,7 @@ PrefillLayout prefill_layout(const jm_layer_dims& d, int64_t T, int32_t n_chunks
 }
 
 struct DecodeLayout {
-  size_t x, z, xh, delta, Bm, Cm, g, total;
+  size_t x, z, xh, delta, Bm, Cm, g, partial, total;
 };
 
 DecodeLayout decode_layout(const jm_layer_dims& d, int64_t b) {
@@ -199,6 +199,9 @@ DecodeLayout decode_layout(const jm_layer_dims& d, int64_t b) {
   L.Bm = take(b * 16 * sizeof(float));
   L.Cm = take(b * 16 * sizeof(float));
   L.g = take(b * di * a);
+  const bool fast = d.act_dtype == JM_BF16 && decode_fast_path_ok(d.d_model, d.d_inner, d.dt_rank);
+  L.partial = take(fast ? decode_fast_partial_floats(d.d_model, d.d_inner, d.dt_rank, 64) * sizeof(float)
+                        : 0);
   L.total = off;
   return L;
 }
@@ -289,6 +292,32 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
   float* Cm = reinterpret_cast<float*>(ws + L.Cm);
   T* g = reinterpret_cast<T*>(ws + L.g);
   const int di = d.d_inner, dm = d.d_model, R = d.dt_rank;
+
+  if constexpr (sizeof(T) == 2) {
+    if (decode_fast_path_ok(dm, di, R)) {
+      float* partial = reinterpret_cast<float*>(ws + L.partial);
+      const bf16* Win = static_cast<const bf16*>(w.in_proj_w);
+      for (int32_t b0 = 0; b0 < b; b0 += 64) {
+        const int M = b - b0 < 64 ? b - b0 : 64;
+        const bf16* ut = u + (int64_t)b0 * dm;
+        bf16* ct = conv_state + (int64_t)b0 * di * 3;
+        float* st = ssm_state + (int64_t)b0 * di * 16;
+        bf16* ot = out + (int64_t)b0 * dm;
+        JM_LAUNCH("dec_in_proj", launch_dec_in_proj(ut, Win, static_cast<const bf16*>(w.conv_w),
+                                                    static_cast<const bf16*>(w.conv_b), ct, xh, z,
+                                                    M, dm, di, stream));
+        JM_LAUNCH("dec_x_proj", launch_dec_x_proj(xh, static_cast<const bf16*>(w.x_proj_w),
+                                                  partial, delta, Bm, Cm, M, di, R, stream));
+        JM_LAUNCH("dec_update", launch_dec_update(xh, z, delta, Bm, Cm,
+                                                  static_cast<const bf16*>(w.dt_proj_w),
+                                                  w.dt_proj_b, w.A_log, w.D, st, g, M, di, R,
+                                                  stream));
+        JM_LAUNCH("dec_out_proj", launch_dec_out_proj(g, static_cast<const bf16*>(w.out_proj_w),
+                                                      partial, ot, M, dm, di, stream));
+      }
+      return ok();
+    }
+  }
 
   EpiArgs e = epi_none();
   e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = di;

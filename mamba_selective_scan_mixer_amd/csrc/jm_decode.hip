@@ -1,0 +1,345 @@
+// Single-token decode of the Mamba mixer layer (bf16 weights/activations, fp32
+// state), for up to 64 sequences per launch.
+//
+// At one token per sequence every projection is a skinny (M <= 64) product whose
+// cost is streaming the weights (210 MB per step at the Jamba-7B-class sizes), so
+// the kernels here are built for bandwidth:
+//   dec_gemm      32 output features per workgroup; each wave takes a K slice and
+//                 loads weight rows and token rows straight into MFMA operand
+//                 registers (no LDS staging): a lane reads 64 contiguous bytes of a
+//                 row, and A and B use the same permutation of k, so the products
+//                 pair up correctly. Partial sums of the waves are combined in LDS
+//                 in a fixed order (deterministic). Optional split-K over a second
+//                 grid dimension writes fp32 partials.
+//   in_proj epilogue: the conv-state shift, the causal conv (kernel 4) and SiLU are
+//                 applied right there for the x half; the z half is stored.
+//   xproj_reduce  sums the split-K partials of x_proj in a fixed order.
+//   update        per 64 channels x 64 sequences: dt_proj on MFMA, softplus, the
+//                 16-state update in place, the D skip and the SiLU(z) gate.
+#include "jm_internal.h"
+
+namespace jm {
+namespace {
+
+constexpr int NS = 16;
+constexpr int DEC_NB = 32;   // output features per workgroup
+constexpr int DEC_MT = 64;   // token rows per launch
+
+enum DecEpi : int { DEC_STORE = 0, DEC_INPROJ_CONV = 1, DEC_PARTIAL = 2 };
+
+struct DecEpiArgs {
+  bf16* out;             // STORE: (M, N) bf16
+  bf16* xh;              // INPROJ: (M, d_inner) conv+SiLU output
+  bf16* z;               // INPROJ: (M, d_inner)
+  bf16* conv_state;      // INPROJ: (M, d_inner, 3) in/out
+  const bf16* conv_w;    // INPROJ: (d_inner, 4)
+  const bf16* conv_b;    // INPROJ: (d_inner) or null
+  int d_inner;           // INPROJ split point
+  float* partial;        // PARTIAL: (splits, M, N) fp32
+};
+
+__device__ __forceinline__ void load64B(const bf16* p, bf16x8 v[4]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4 r = q[j];
+    v[j] = *reinterpret_cast<bf16x8*>(&r);
+  }
+}
+
+template <int WAVES, int FB, int EPI>
+__global__ __launch_bounds__(64 * WAVES)
+void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int M, int N, int K,
+                     int k_per_split, DecEpiArgs e) {
+  constexpr int NB = 32 * FB;                   // output features per workgroup
+  __shared__ float red[WAVES][FB * 2][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * NB;
+  const int split = blockIdx.y;
+  const int kbeg = split * k_per_split;
+  const int kw = k_per_split / WAVES;          // multiple of 64
+  const int ka = kbeg + wave * kw;
+  const int lrow = lane & 31;
+  const int half = lane >> 5;
+
+  const bf16* wp[FB];
+#pragma unroll
+  for (int f = 0; f < FB; ++f) {
+    int wrow = n0 + f * 32 + lrow;
+    if (wrow >= N) wrow = N - 1;               // clamped rows are never stored
+    wp[f] = W + (int64_t)wrow * K + ka + half * 32;
+  }
+  // Token rows past M read row 0 instead: an MFMA output column depends only on
+  // its own token's operand, and columns >= M are never stored.
+  const int t0 = lrow, t1 = lrow + 32;
+  const bf16* up0 = U + (int64_t)(t0 < M ? t0 : 0) * K + ka + half * 32;
+  const bf16* up1 = U + (int64_t)(t1 < M ? t1 : 0) * K + ka + half * 32;
+
+  f32x16 acc[FB][2];
+#pragma unroll
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { acc[f][0][r] = 0.0f; acc[f][1][r] = 0.0f; }
+  // Register double buffer: the loads of block i+1 are in flight while block i's
+  // MFMAs run. The steady-state loop has no branches, so the compiler can wait for
+  // exactly the older buffer (kw / 64 is even by construction).
+  struct Buf { bf16x8 w[FB][4], a[4], b[4]; };
+  // Workgroups walk their K slice starting at different 64-wide blocks, so the
+  // token rows (shared by every workgroup, served from L2) are not all requested
+  // from the same few cache lines at the same moment.
+  const int nblk = kw >> 6;
+  const int rot = blockIdx.x % nblk;
+  auto load = [&](Buf& B, int kk) {
+    int blk = (kk >> 6) + rot;
+    if (blk >= nblk) blk -= nblk;
+    const int ko = blk << 6;
+#pragma unroll
+    for (int f = 0; f < FB; ++f) load64B(wp[f] + ko, B.w[f]);
+    load64B(up0 + ko, B.a);
+    load64B(up1 + ko, B.b);
+  };
+  auto compute = [&](const Buf& B) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int f = 0; f < FB; ++f) {
+        acc[f][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B.w[f][j], B.a[j], acc[f][0], 0, 0, 0);
+        acc[f][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B.w[f][j], B.b[j], acc[f][1], 0, 0, 0);
+      }
+  };
+  constexpr int NLOAD = FB * 4 + 8;   // 16-byte loads per block
+  constexpr int NMFMA = FB * 8;       // MFMAs per block
+  Buf b0, b1;
+  load(b0, 0);
+  int kk = 0;
+  for (; kk + 128 < kw; kk += 128) {
+    load(b1, kk + 64);
+    compute(b0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NLOAD, 0);   // next block's loads first
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);   // then this block's MFMAs
+    load(b0, kk + 128);
+    compute(b1);
+    __builtin_amdgcn_sched_group_barrier(0x020, NLOAD, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+  }
+  load(b1, kk + 64);
+  compute(b0);
+  compute(b1);
+#pragma unroll
+  for (int f = 0; f < FB; ++f)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      red[wave][2 * f][r][lane] = acc[f][0][r];
+      red[wave][2 * f + 1][r][lane] = acc[f][1][r];
+    }
+  __syncthreads();
+  // FB x 2 x 16 x 64 outputs; block (f, tb), register r, lane l:
+  // feature n0 + 32 f + 8(r/4) + 4(l/32) + r%4, token l%32 + 32 tb.
+  for (int o = threadIdx.x; o < FB * 2048; o += 64 * WAVES) {
+    const int blk = o >> 10, r = (o >> 6) & 15, l = o & 63;
+    const int f = blk >> 1, tb = blk & 1;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += red[w][blk][r][l];
+    const int m = (l & 31) + 32 * tb;
+    const int n = n0 + 32 * f + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    if (m >= M || n >= N) continue;
+    if constexpr (EPI == DEC_STORE) {
+      e.out[(int64_t)m * N + n] = from_f32<bf16>(v);
+    } else if constexpr (EPI == DEC_PARTIAL) {
+      e.partial[((int64_t)split * M + m) * N + n] = v;
+    } else {
+      const int di = e.d_inner;
+      if (n < di) {
+        bf16* st = e.conv_state + ((int64_t)m * di + n) * 3;
+        const bf16 xb = from_f32<bf16>(v);
+        const float s0 = to_f32(st[0]), s1 = to_f32(st[1]), s2 = to_f32(st[2]);
+        const bf16* cw = e.conv_w + (int64_t)n * 4;
+        float c = e.conv_b ? to_f32(e.conv_b[n]) : 0.0f;
+        c = fmaf(to_f32(cw[0]), s0, c);
+        c = fmaf(to_f32(cw[1]), s1, c);
+        c = fmaf(to_f32(cw[2]), s2, c);
+        c = fmaf(to_f32(cw[3]), to_f32(xb), c);
+        e.xh[(int64_t)m * di + n] = from_f32<bf16>(silu(c));
+        st[0] = st[1];
+        st[1] = st[2];
+        st[2] = xb;
+      } else {
+        e.z[(int64_t)m * di + (n - di)] = from_f32<bf16>(v);
+      }
+    }
+  }
+}
+
+// out = bf16(sum of split-K partials), fixed order.
+__global__ __launch_bounds__(256)
+void dec_sum_partials_kernel(const float* __restrict__ partial, int splits, int64_t count,
+                             bf16* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= count) return;
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += partial[s * count + idx];
+  out[idx] = from_f32<bf16>(v);
+}
+
+// Sum split-K partials of x_proj in a fixed order: delta (bf16), B and C (fp32).
+__global__ __launch_bounds__(256)
+void dec_xproj_reduce_kernel(const float* __restrict__ partial, int splits, int M, int R,
+                             bf16* __restrict__ delta, float* __restrict__ Bm,
+                             float* __restrict__ Cm) {
+  const int N = R + 2 * NS;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * N) return;
+  const int m = idx / N, n = idx % N;
+  float v = 0.0f;
+  for (int s = 0; s < splits; ++s) v += partial[((int64_t)s * M + m) * N + n];
+  if (n < R) delta[(int64_t)m * R + n] = from_f32<bf16>(v);
+  else if (n < R + NS) Bm[m * NS + (n - R)] = v;
+  else Cm[m * NS + (n - R - NS)] = v;
+}
+
+// dt_proj (MFMA) + softplus + state update + D skip + gate for 32 channels x 64 tokens.
+// Waves 0/1 take tokens 0-31/32-63 over the first half of dt_rank, waves 2/3 the
+// second half; the two halves are added in LDS.
+constexpr int UPD_CH = 32;
+__global__ __launch_bounds__(256)
+void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
+                       const bf16* __restrict__ delta, const float* __restrict__ Bm,
+                       const float* __restrict__ Cm, const bf16* __restrict__ W_dt,
+                       const float* __restrict__ b_dt, const float* __restrict__ A_log,
+                       const float* __restrict__ Dv, float* __restrict__ state,
+                       bf16* __restrict__ g, int M, int d_inner, int R) {
+  __shared__ float sdt[2][DEC_MT][UPD_CH + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int d0 = blockIdx.x * UPD_CH;
+  const int lrow = lane & 31, half = lane >> 5;
+  {
+    const int tb = wave & 1, kh = wave >> 1;
+    const int tok = tb * 32 + lrow;   // rows >= M read row 0; their results are unused
+    const bool tv = tok < M;
+    const int kq = R / 4;                       // k range of one lane: kh half, lane half
+    const int kbase = kh * (R / 2) + half * kq;
+    const bf16* dp = delta + (int64_t)(tv ? tok : 0) * R + kbase;
+    const bf16* wp = W_dt + (int64_t)(d0 + lrow) * R + kbase;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    for (int kk = 0; kk < kq; kk += 32) {
+      bf16x8 a[4], w[4];
+      load64B(dp + kk, a);
+      load64B(wp + kk, w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[j], a[j], acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sdt[kh][tb * 32 + lrow][8 * (r >> 2) + 4 * half + (r & 3)] = acc[r];
+  }
+  __syncthreads();
+  const int c = lane & (UPD_CH - 1);
+  const int d = d0 + c;
+  const int msub = (wave << 1) | (lane >> 5);   // 0..7
+  float a2[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) a2[n] = -fast_exp(A_log[(int64_t)d * NS + n]) * kLog2e;
+  const float Dd = Dv[d];
+  const float bias = b_dt[d];
+  for (int m = msub; m < M; m += 8) {
+    const int64_t o = (int64_t)m * d_inner + d;
+    const float dtv = softplus(sdt[0][m][c] + sdt[1][m][c] + bias);
+    const float xv = to_f32(xh[o]);
+    const float zv = to_f32(z[o]);
+    const float dx = dtv * xv;
+    float4* st = reinterpret_cast<float4*>(state + o * NS);
+    float h[NS];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = st[q];
+      h[4 * q] = f.x; h[4 * q + 1] = f.y; h[4 * q + 2] = f.z; h[4 * q + 3] = f.w;
+    }
+    const float* bb = Bm + m * NS;
+    const float* cc = Cm + m * NS;
+    float y = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * bb[n]);
+      y = fmaf(cc[n], h[n], y);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+    y = fmaf(Dd, xv, y);
+    g[o] = from_f32<bf16>(y * silu(zv));
+  }
+}
+
+template <int WAVES, int FB, int EPI>
+hipError_t launch_dec_gemm(const bf16* U, const bf16* W, int M, int N, int K, int splits,
+                           const DecEpiArgs& e, hipStream_t s) {
+  dim3 grid((N + 32 * FB - 1) / (32 * FB), splits);
+  hipLaunchKernelGGL((dec_gemm_kernel<WAVES, FB, EPI>), grid, dim3(64 * WAVES), 0, s, U, W, M, N,
+                     K, K / splits, e);
+  return hipGetLastError();
+}
+
+constexpr int XPROJ_SPLIT_K = 512;   // K per workgroup for x_proj
+constexpr int OUTPROJ_SPLITS = 4;
+
+}  // namespace
+
+bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank) {
+  return d_model % 256 == 0 && d_inner % 1024 == 0 && dt_rank % 128 == 0;
+}
+
+size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile) {
+  const size_t xp = (size_t)(d_inner / XPROJ_SPLIT_K) * batch_tile * (dt_rank + 2 * NS);
+  const size_t op = (size_t)OUTPROJ_SPLITS * batch_tile * d_model;
+  return xp > op ? xp : op;
+}
+
+hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
+                              const bf16* conv_b, bf16* conv_state, bf16* xh, bf16* z, int M,
+                              int d_model, int d_inner, hipStream_t s) {
+  DecEpiArgs e = {};
+  e.xh = xh; e.z = z; e.conv_state = conv_state; e.conv_w = conv_w; e.conv_b = conv_b;
+  e.d_inner = d_inner;
+  return launch_dec_gemm<4, 2, DEC_INPROJ_CONV>(u, W_in, M, 2 * d_inner, d_model, 1, e, s);
+}
+
+hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf16* delta,
+                             float* Bm, float* Cm, int M, int d_inner, int dt_rank,
+                             hipStream_t s) {
+  const int N = dt_rank + 2 * NS;
+  const int splits = d_inner / XPROJ_SPLIT_K;   // 128-deep K slice per wave
+  DecEpiArgs e = {};
+  e.partial = partial;
+  hipError_t err = launch_dec_gemm<4, 1, DEC_PARTIAL>(xh, W_x, M, N, d_inner, splits, e, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dec_xproj_reduce_kernel, dim3((M * N + 255) / 256), dim3(256), 0, s,
+                     partial, splits, M, dt_rank, delta, Bm, Cm);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, const float* Bm,
+                             const float* Cm, const bf16* W_dt, const float* b_dt,
+                             const float* A_log, const float* D, float* ssm_state, bf16* g, int M,
+                             int d_inner, int dt_rank, hipStream_t s) {
+  hipLaunchKernelGGL(dec_update_kernel, dim3(d_inner / UPD_CH), dim3(256), 0, s, xh, z, delta, Bm,
+                     Cm, W_dt, b_dt, A_log, D, ssm_state, g, M, d_inner, dt_rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, bf16* out, int M,
+                               int d_model, int d_inner, hipStream_t s) {
+  DecEpiArgs e = {};
+  e.partial = partial;
+  hipError_t err = launch_dec_gemm<4, 2, DEC_PARTIAL>(g, W_out, M, d_model, d_inner,
+                                                      OUTPROJ_SPLITS, e, s);
+  if (err != hipSuccess) return err;
+  const int64_t count = (int64_t)M * d_model;
+  hipLaunchKernelGGL(dec_sum_partials_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                     s, partial, OUTPROJ_SPLITS, count, out);
+  return hipGetLastError();
+}
+
+}  // namespace jm

@@ -106,4 +106,19 @@ hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const f
                                 const float* A_log, const float* D, float* ssm_state, T* g,
                                 int batch, int d_inner, int dt_rank, hipStream_t s);
 
+// Decode fast path (bf16; d_model % 256, d_inner % 1024, dt_rank % 128; <= 64 rows per launch).
+bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank);
+size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile);
+hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
+                              const bf16* conv_b, bf16* conv_state, bf16* xh, bf16* z, int M,
+                              int d_model, int d_inner, hipStream_t s);
+hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf16* delta,
+                             float* Bm, float* Cm, int M, int d_inner, int dt_rank, hipStream_t s);
+hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, const float* Bm,
+                             const float* Cm, const bf16* W_dt, const float* b_dt,
+                             const float* A_log, const float* D, float* ssm_state, bf16* g, int M,
+                             int d_inner, int dt_rank, hipStream_t s);
+hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, bf16* out, int M,
+                               int d_model, int d_inner, hipStream_t s);
+
 }  // namespace jm

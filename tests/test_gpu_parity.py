@@ -139,8 +139,9 @@ def test_causal_bitwise():
         assert np.array_equal(got[0][:t + 1], base[0][:t + 1]), t
 
 
-def _decode_case(wl, steps, tol):
+def _decode_case(wl, steps, tol, state_tol=None):
     """Prefill (oracle and GPU each from their own prefill), then decode steps."""
+    state_tol = tol if state_tol is None else state_tol
     w64 = oracle.as_f64(wl.weights)
     ref = oracle.prefill(w64, wl.u, wl.cu_seqlens)
     layer = device_layer(wl)
@@ -156,7 +157,7 @@ def _decode_case(wl, steps, tol):
         torch.cuda.synchronize()
         e = (rel_err(to_np(out_g), out_r), rel_err(to_np(conv_d), conv_r), rel_err(to_np(ssm_d), ssm_r))
         worst = max(worst, *e)
-        assert max(e) < tol, (s, e)
+        assert e[0] < tol and e[1] < state_tol and e[2] < state_tol, (s, e)
     print(f"decode worst error {worst:.2e}", flush=True)
 
 
@@ -171,6 +172,25 @@ def test_decode_tiny_fp32(D_value):
 def test_decode_jamba_bf16(D_value):
     wl = synth.make_workload("decode_b64", batch=3, prefill_len=20, steps=6, D_value=D_value)
     _decode_case(wl, 6, TOL["bf16"])
+
+
+def test_decode_tiny_bf16_generic_path():
+    """bf16 at widths the fast decode kernels do not take (generic kernels).
+
+    Not one of the Jamba-width workloads the 2e-2 bound is stated for: at 128
+    channels with D = 0 the output is a short, cancelling sum C.h, and a numpy
+    model that only rounds x, z, x^, delta, g and out to bf16 (everything else
+    fp64) already reaches 2.4e-2 at step 2 of this very input. So `out` is held to
+    5e-2 here and the carried states to the usual 2e-2."""
+    wl = synth.make_workload("decode_b64", dims=synth.TINY_DIMS, dtype="bf16", batch=4,
+                             prefill_len=9, steps=5, D_value=0.0)
+    _decode_case(wl, 5, 5e-2, state_tol=TOL["bf16"])
+
+
+def test_decode_jamba_bf16_two_batch_tiles():
+    """Batch 70 > 64: the fast path runs two row tiles per step."""
+    wl = synth.make_workload("decode_b64", batch=70, prefill_len=3, steps=2, D_value=0.0)
+    _decode_case(wl, 2, TOL["bf16"])
 
 
 def test_prefill_state_equals_repeated_decode_fp32():

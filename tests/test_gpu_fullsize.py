@@ -1,0 +1,174 @@
+"""Full-size parity: every workload at its full size, in the launch configuration the
+benchmark uses (automatic chunk plan, 64-row decode tiles), compared with the fp64 CPU
+oracle on outputs the oracle can compute in seconds:
+
+  prefill_4k     the whole layer, D = 1 and D = 0;
+  prefill_128k   (a) the first 256 rows of the real input (rows depend only on earlier
+                 tokens); (b) a constructed input of the same size - random first and last
+                 512 tokens, zeros in between - where every middle row must be exactly 0
+                 (z = 0 so the gate is 0) and the last 512 rows and the final states must
+                 match the oracle started from the closed-form fixed point of the
+                 zero-input recurrence, h* = Delta B x^ / (1 - exp(Delta A)) (after 130K
+                 zero tokens the prefix has decayed by at most e^-123);
+  decode_b64     2048-token prefill for 64 sequences, 1024 decode steps; two sampled
+                 sequences checked against the oracle at every step (out) and at steps
+                 1, 32 and 1024 (states);
+  packed_varlen  16 sequences of 1024..8192 tokens; three whole sequences, the first 64
+                 rows of every sequence and the final states of the sampled sequences.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from jm_testutil import TOL, device_layer, rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+jm = pytest.importorskip("mamba_selective_scan_mixer_amd")
+
+
+@pytest.fixture(autouse=True)
+def _auto_chunk():
+    jm.set_scan_chunk_len(0)
+    yield
+
+
+def run_prefill(layer, u_np, cu, dtype="bf16"):
+    u = to_dev(u_np, dtype)
+    cu_d = torch.as_tensor(np.asarray(cu, np.int32)).cuda()
+    out, conv, ssm = jm.jamba_mamba_prefill(layer, u, cu_d, [int(v) for v in cu])
+    torch.cuda.synchronize()
+    del u
+    return out, conv, ssm
+
+
+def report(label, **errs):
+    print(label + " " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("D_value", [1.0, 0.0])
+def test_prefill_4k_full(D_value):
+    wl = synth.make_workload("prefill_4k", D_value=D_value)
+    layer = device_layer(wl)
+    out, conv, ssm = run_prefill(layer, wl.u, wl.cu_seqlens)
+    ref = oracle.prefill(wl.weights, wl.u, wl.cu_seqlens)
+    e = dict(out=rel_err(to_np(out), ref["out"]), conv=rel_err(to_np(conv), ref["conv_state"]),
+             ssm=rel_err(to_np(ssm), ref["ssm_state"]))
+    report(f"prefill_4k D={D_value}", **e)
+    assert max(e.values()) < TOL["bf16"], e
+
+
+def test_prefill_128k_real_input_prefix():
+    wl = synth.make_workload("prefill_128k", D_value=0.0)
+    layer = device_layer(wl)
+    out, _, _ = run_prefill(layer, wl.u, wl.cu_seqlens)
+    head = to_np(out[:256])
+    ref = oracle.prefill(wl.weights, wl.u[:256], [0, 256])
+    e = rel_err(head, ref["out"])
+    report("prefill_128k real-input rows 0..255", out=e)
+    assert e < TOL["bf16"]
+
+
+def zero_input_fixed_point(w64):
+    """Closed-form limit of the SSM state under a long run of zero input tokens."""
+    di = w64["D"].shape[0]
+    N = w64["A_log"].shape[1]
+    R = w64["dt_proj_w"].shape[1]
+    x_hat0, _ = oracle.causal_conv_silu(np.zeros((1, di)), w64["conv_w"], w64["conv_b"], None)
+    delta0, B0, _ = oracle.x_proj(x_hat0, w64["x_proj_w"], R, N)
+    dt0 = oracle.dt_proj(delta0, w64["dt_proj_w"], w64["dt_proj_b"])[0]       # (di,)
+    a = np.exp(dt0[:, None] * (-np.exp(w64["A_log"])))                       # (di, N)
+    b = dt0[:, None] * B0[0][None, :] * x_hat0[0][:, None]
+    return b / (1.0 - a), a
+
+
+@pytest.mark.parametrize("D_value", [1.0, 0.0])
+def test_prefill_128k_constructed_input(D_value):
+    wl = synth.make_workload("prefill_128k", D_value=D_value)
+    T = wl.total_tokens
+    P = 512
+    u = wl.u.copy()
+    u[P:T - P] = 0.0
+    layer = device_layer(wl)
+    out, conv, ssm = run_prefill(layer, u, wl.cu_seqlens)
+    w64 = oracle.as_f64(wl.weights)
+    # (a) head rows
+    ref_head = oracle.prefill(w64, u[:P], [0, P])
+    e_head = rel_err(to_np(out[:P]), ref_head["out"])
+    # (b) the zero stretch gives exactly zero output rows
+    mid = out[P:T - P]
+    n_nonzero = int(torch.count_nonzero(mid).item())
+    # (c) tail rows and final states from the fixed point
+    h_star, a = zero_input_fixed_point(w64)
+    assert np.max(a) ** (T - 2 * P) < 1e-40      # the head is forgotten
+    di = w64["D"].shape[0]
+    ref_tail = oracle.prefill(w64, u[T - P:], [0, P], init_conv=np.zeros((1, di, 3)),
+                              init_ssm=h_star[None])
+    e = dict(head=e_head, tail=rel_err(to_np(out[T - P:]), ref_tail["out"]),
+             conv=rel_err(to_np(conv), ref_tail["conv_state"]),
+             ssm=rel_err(to_np(ssm), ref_tail["ssm_state"]))
+    report(f"prefill_128k constructed D={D_value} nonzero_mid={n_nonzero}", **e)
+    assert n_nonzero == 0
+    assert max(e.values()) < TOL["bf16"], e
+
+
+@pytest.mark.parametrize("D_value", [0.0, 1.0])
+def test_decode_b64_full(D_value):
+    steps = 1024 if D_value == 0.0 else 64
+    wl = synth.make_workload("decode_b64", D_value=D_value, steps=steps)
+    B = wl.n_seqs
+    layer = device_layer(wl)
+    _, conv, ssm = run_prefill(layer, wl.u, wl.cu_seqlens)
+    sample = [0, 37]
+    w64 = oracle.as_f64(wl.weights)
+    cu = wl.cu_seqlens
+    ref = oracle.prefill(w64, np.concatenate([wl.u[cu[i]:cu[i + 1]] for i in sample]),
+                         [0, 2048, 4096])
+    conv_r, ssm_r = ref["conv_state"], ref["ssm_state"]
+    out = torch.empty((B, wl.dims.d_model), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(jm.decode_workspace_size(layer.dims, B), dtype=torch.uint8, device="cuda")
+    worst = {"out": 0.0, "conv": 0.0, "ssm": 0.0}
+    for s in range(1, steps + 1):
+        tok = wl.next_decode_tokens()
+        jm.jamba_mamba_decode_step(layer, to_dev(tok, "bf16"), conv, ssm, out=out, workspace=ws)
+        out_r, conv_r, ssm_r = oracle.decode_step(w64, tok[sample], conv_r, ssm_r)
+        e_out = rel_err(to_np(out[sample]), out_r)
+        worst["out"] = max(worst["out"], e_out)
+        assert e_out < TOL["bf16"], (s, e_out)
+        if s % 256 == 0:
+            print(f"decode_b64 D={D_value}: step {s}/{steps} worst out so far {worst['out']:.2e}",
+                  flush=True)
+        if s in (1, 32, steps):
+            e_c = rel_err(to_np(conv[sample]), conv_r)
+            e_s = rel_err(to_np(ssm[sample]), ssm_r)
+            worst["conv"] = max(worst["conv"], e_c)
+            worst["ssm"] = max(worst["ssm"], e_s)
+            report(f"decode_b64 D={D_value} step {s}", out=e_out, conv=e_c, ssm=e_s)
+            assert e_c < TOL["bf16"] and e_s < TOL["bf16"], (s, e_c, e_s)
+    report(f"decode_b64 D={D_value} worst over {steps} steps", **worst)
+
+
+@pytest.mark.parametrize("D_value", [1.0, 0.0])
+def test_packed_varlen_full(D_value):
+    wl = synth.make_workload("packed_varlen", D_value=D_value)
+    layer = device_layer(wl)
+    out, conv, ssm = run_prefill(layer, wl.u, wl.cu_seqlens)
+    cu = wl.cu_seqlens
+    w64 = oracle.as_f64(wl.weights)
+    order = np.argsort(wl.lengths)
+    whole = [int(order[0]), int(order[1]), int(order[-1])]   # two shortest and the longest
+    errs = {}
+    for i in whole:
+        s, e = int(cu[i]), int(cu[i + 1])
+        ref = oracle.prefill(w64, wl.u[s:e], [0, e - s])
+        errs[f"seq{i}_out"] = rel_err(to_np(out[s:e]), ref["out"])
+        errs[f"seq{i}_conv"] = rel_err(to_np(conv[i]), ref["conv_state"][0])
+        errs[f"seq{i}_ssm"] = rel_err(to_np(ssm[i]), ref["ssm_state"][0])
+    heads = np.concatenate([wl.u[cu[i]:cu[i] + 64] for i in range(wl.n_seqs)])
+    ref_heads = oracle.prefill(w64, heads, np.arange(0, 64 * wl.n_seqs + 1, 64))
+    got_heads = np.concatenate([to_np(out[int(cu[i]):int(cu[i]) + 64]) for i in range(wl.n_seqs)])
+    errs["heads_out"] = rel_err(got_heads, ref_heads["out"])
+    report(f"packed_varlen D={D_value} lengths={wl.lengths}", **errs)
+    assert max(errs.values()) < TOL["bf16"], errs

@@ -26,6 +26,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+# fp32 VALU issue rate without packed math: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# issue slots per SSM state update: mul, exp2 (~2 slots on gfx950), mul, fma (+ fma for y)
+SCAN_SLOTS = {"scan_chunk_state": 5.0, "scan_chunk_output": 6.0}
 METRIC = "Mamba-layer prefill tok/s @128K, decode tok/s @B=64; % HBM/MFMA peak"
 
 
@@ -186,6 +190,11 @@ def main():
              "tflops": round(flops / (avg * 1e-3) / 1e12, 1) if flops else None}
         b = bound_of(name)
         k["bound"] = b
+        if name in SCAN_SLOTS:
+            updates = float(T) * d.d_inner * 16
+            if name == "scan_chunk_state":
+                updates *= (nc - 1) / nc      # the last chunk needs no aggregate
+            k["alu_frac"] = round(updates * SCAN_SLOTS[name] / VALU_LANE_OPS / (avg * 1e-3), 4)
         if b == "mfma":
             k["frac"] = round(k["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
         elif k["gbs"] is not None:

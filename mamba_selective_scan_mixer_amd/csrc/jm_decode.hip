@@ -110,22 +110,38 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
   };
   constexpr int NLOAD = FB * 4 + 8;   // 16-byte loads per block
   constexpr int NMFMA = FB * 8;       // MFMAs per block
-  Buf b0, b1;
-  load(b0, 0);
-  int kk = 0;
-  for (; kk + 128 < kw; kk += 128) {
-    load(b1, kk + 64);
-    compute(b0);
-    __builtin_amdgcn_sched_group_barrier(0x020, NLOAD, 0);   // next block's loads first
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);   // then this block's MFMAs
-    load(b0, kk + 128);
-    compute(b1);
+  auto order = [&]() {                // next blocks' loads first, then this block's MFMAs
     __builtin_amdgcn_sched_group_barrier(0x020, NLOAD, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
+  };
+  const int nb = kw >> 6;
+  if (nb % 4 == 0) {
+    // Four register buffers: blocks i+1..i+3 are in flight while block i computes.
+    Buf b0, b1, b2, b3;
+    load(b0, 0); load(b1, 64); load(b2, 128);
+    int i = 0;
+    for (; i + 4 < nb; i += 4) {
+      const int k0 = i << 6;
+      load(b3, k0 + 192); compute(b0); order();
+      load(b0, k0 + 256); compute(b1); order();
+      load(b1, k0 + 320); compute(b2); order();
+      load(b2, k0 + 384); compute(b3); order();
+    }
+    load(b3, (i << 6) + 192);
+    compute(b0); compute(b1); compute(b2); compute(b3);
+  } else {
+    // Two register buffers (nb is even).
+    Buf b0, b1;
+    load(b0, 0);
+    int kk = 0;
+    for (; kk + 128 < kw; kk += 128) {
+      load(b1, kk + 64); compute(b0); order();
+      load(b0, kk + 128); compute(b1); order();
+    }
+    load(b1, kk + 64);
+    compute(b0);
+    compute(b1);
   }
-  load(b1, kk + 64);
-  compute(b0);
-  compute(b1);
 #pragma unroll
   for (int f = 0; f < FB; ++f)
 #pragma unroll
@@ -199,10 +215,13 @@ void dec_xproj_reduce_kernel(const float* __restrict__ partial, int splits, int 
   else Cm[m * NS + (n - R - NS)] = v;
 }
 
-// dt_proj (MFMA) + softplus + state update + D skip + gate for 32 channels x 64 tokens.
-// Waves 0/1 take tokens 0-31/32-63 over the first half of dt_rank, waves 2/3 the
-// second half; the two halves are added in LDS.
+// dt_proj (MFMA) + softplus + state update + D skip + gate for 32 channels x 32 tokens
+// (grid.y takes the token halves of a 64-row tile, so a 64-row step runs 2 d_inner/32
+// workgroups). Wave w computes the 32x32 dt tile over the w-th quarter of dt_rank; the
+// four partial tiles are added in LDS. In the update, lane l takes channel l % 32 and
+// one token at a time, with its 16 states in registers (four 16-byte loads in flight).
 constexpr int UPD_CH = 32;
+constexpr int UPD_MT = 32;
 __global__ __launch_bounds__(256)
 void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
                        const bf16* __restrict__ delta, const float* __restrict__ Bm,
@@ -210,44 +229,43 @@ void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
                        const float* __restrict__ b_dt, const float* __restrict__ A_log,
                        const float* __restrict__ Dv, float* __restrict__ state,
                        bf16* __restrict__ g, int M, int d_inner, int R) {
-  __shared__ float sdt[2][DEC_MT][UPD_CH + 1];
+  __shared__ float sdt[4][UPD_MT][UPD_CH + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int d0 = blockIdx.x * UPD_CH;
-  const int lrow = lane & 31, half = lane >> 5;
+  const int m0 = blockIdx.y * UPD_MT;
   {
-    const int tb = wave & 1, kh = wave >> 1;
-    const int tok = tb * 32 + lrow;   // rows >= M read row 0; their results are unused
-    const bool tv = tok < M;
-    const int kq = R / 4;                       // k range of one lane: kh half, lane half
-    const int kbase = kh * (R / 2) + half * kq;
-    const bf16* dp = delta + (int64_t)(tv ? tok : 0) * R + kbase;
-    const bf16* wp = W_dt + (int64_t)(d0 + lrow) * R + kbase;
+    const int lrow = lane & 31, half = lane >> 5;
+    const int tok = m0 + lrow;              // rows >= M read row 0; their results are unused
+    const int kq = R / 4;                   // this wave's share of dt_rank
+    const bf16* dp = delta + (int64_t)(tok < M ? tok : 0) * R + wave * kq + 8 * half;
+    const bf16* wp = W_dt + (int64_t)(d0 + lrow) * R + wave * kq + 8 * half;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    for (int kk = 0; kk < kq; kk += 32) {
-      bf16x8 a[4], w[4];
-      load64B(dp + kk, a);
-      load64B(wp + kk, w);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[j], a[j], acc, 0, 0, 0);
+    for (int kk = 0; kk < kq; kk += 16) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(dp + kk);
+      const bf16x8 w = *reinterpret_cast<const bf16x8*>(wp + kk);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, acc, 0, 0, 0);
     }
+    // acc row = channel, column = token
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sdt[kh][tb * 32 + lrow][8 * (r >> 2) + 4 * half + (r & 3)] = acc[r];
+    for (int r = 0; r < 16; ++r) sdt[wave][lrow][8 * (r >> 2) + 4 * half + (r & 3)] = acc[r];
   }
   __syncthreads();
   const int c = lane & (UPD_CH - 1);
   const int d = d0 + c;
-  const int msub = (wave << 1) | (lane >> 5);   // 0..7
   float a2[NS];
 #pragma unroll
   for (int n = 0; n < NS; ++n) a2[n] = -fast_exp(A_log[(int64_t)d * NS + n]) * kLog2e;
   const float Dd = Dv[d];
   const float bias = b_dt[d];
-  for (int m = msub; m < M; m += 8) {
+  const int mend = min(M - m0, UPD_MT);
+  for (int ml = (wave << 1) | (lane >> 5); ml < mend; ml += 8) {
+    const int m = m0 + ml;
     const int64_t o = (int64_t)m * d_inner + d;
-    const float dtv = softplus(sdt[0][m][c] + sdt[1][m][c] + bias);
+    const float dtv =
+        softplus(((sdt[0][ml][c] + sdt[1][ml][c]) + (sdt[2][ml][c] + sdt[3][ml][c])) + bias);
     const float xv = to_f32(xh[o]);
     const float zv = to_f32(z[o]);
     const float dx = dtv * xv;
@@ -324,7 +342,8 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
                              const float* Cm, const bf16* W_dt, const float* b_dt,
                              const float* A_log, const float* D, float* ssm_state, bf16* g, int M,
                              int d_inner, int dt_rank, hipStream_t s) {
-  hipLaunchKernelGGL(dec_update_kernel, dim3(d_inner / UPD_CH), dim3(256), 0, s, xh, z, delta, Bm,
+  hipLaunchKernelGGL(dec_update_kernel, dim3(d_inner / UPD_CH, (M + UPD_MT - 1) / UPD_MT),
+                     dim3(256), 0, s, xh, z, delta, Bm,
                      Cm, W_dt, b_dt, A_log, D, ssm_state, g, M, d_inner, dt_rank);
   return hipGetLastError();
 }

@@ -27,8 +27,11 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf
 // ---- activations (fp32) --------------------------------------------------------
 // exp(v) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float v) { return __builtin_amdgcn_exp2f(v * kLog2e); }
-// SiLU(v) = v * sigmoid(v).
-__device__ __forceinline__ float silu(float v) { return v / (1.0f + fast_exp(-v)); }
+// SiLU(v) = v * sigmoid(v), with the hardware reciprocal (about 1 ulp) in place of an
+// IEEE division.
+__device__ __forceinline__ float silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + fast_exp(-v));
+}
 // log1p(x) for x in [0, 1] with hardware log2: Kahan's identity
 // log1p(x) = x * ln(u) / (u - 1), u = fl(1 + x), which cancels the rounding of
 // 1 + x and keeps a few-ulp relative error even when x is tiny (u == 1 -> x).

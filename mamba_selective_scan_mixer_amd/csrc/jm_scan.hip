@@ -80,14 +80,26 @@ void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ 
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
     }
     const int64_t e = s_end < t1 ? s_end : t1;
-    for (; t < e; ++t) {
-      const float dtv = dt[t * d_inner + d];
-      const float dx = dtv * to_f32(x[t * d_inner + d]);
-      const float* b = Bm + t * NS;
+    // Two tokens per iteration with alternating state registers (no copies).
+    auto step = [&](int64_t tc, const float (&hin)[NS], float (&hout)[NS]) {
+      const float dtv = dt[tc * d_inner + d];
+      const float dx = dtv * to_f32(x[tc * d_inner + d]);
+      const float* b = Bm + tc * NS;
 #pragma unroll
       for (int n = 0; n < NS; ++n)
-        h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * b[n]);
+        hout[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), hin[n], dx * b[n]);
       dsum += dtv;
+    };
+    float h2[NS];
+    for (; t + 1 < e; t += 2) {
+      step(t, h, h2);
+      step(t + 1, h2, h);
+    }
+    if (t < e) {
+      step(t, h, h2);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h[n] = h2[n];
+      ++t;
     }
     ++i;
   }
@@ -147,22 +159,34 @@ void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
     }
     const int64_t e = s_end < t1 ? s_end : t1;
-    for (; t < e; ++t) {
-      const int64_t o = t * d_inner + d;
+    // Two tokens per iteration: the state alternates between h and h2, so the
+    // loop-carried registers need no copies.
+    auto step = [&](int64_t tc, const float (&hin)[NS], float (&hout)[NS]) {
+      const int64_t o = tc * d_inner + d;
       const float dtv = dt[o];
       const float xv = to_f32(x[o]);
       const float zv = to_f32(z[o]);
       const float dx = dtv * xv;
-      const float* b = Bm + t * NS;
-      const float* c = Cm + t * NS;
-      float y = 0.0f;
+      const float* b = Bm + tc * NS;
+      const float* c = Cm + tc * NS;
+      float y = Dd * xv;
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
-        h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * b[n]);
-        y = fmaf(c[n], h[n], y);
+        hout[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), hin[n], dx * b[n]);
+        y = fmaf(c[n], hout[n], y);
       }
-      y = fmaf(Dd, xv, y);
       g[o] = from_f32<T>(y * silu(zv));
+    };
+    float h2[NS];
+    for (; t + 1 < e; t += 2) {
+      step(t, h, h2);
+      step(t + 1, h2, h);
+    }
+    if (t < e) {
+      step(t, h, h2);
+#pragma unroll
+      for (int n = 0; n < NS; ++n) h[n] = h2[n];
+      ++t;
     }
     if (e == s_end && final_state) store16(final_state + ((int64_t)i * d_inner + d) * NS, h);
     ++i;

@@ -460,9 +460,108 @@ void gemm_f32_kernel(const float* __restrict__ X, int64_t ldx,
   }
 }
 
+// ---- dt_proj + bias + softplus (bf16 in, fp32 out) -----------------------------------
+// Delta[t, d] = softplus(sum_k delta[t, k] * W[d, k] + b[d]) for dt_rank K = 128 or 256.
+// The fp32 output (8x the bytes of the input row) makes this a store- and VALU-bound
+// kernel, so it is shaped for the stores rather than for the MFMAs:
+//   * a workgroup = 4 waves = 128 channels; wave w keeps the weight rows of channels
+//     32w..32w+31 in registers for its whole life (MFMA B operand: lane -> channel
+//     lane % 32, k half lane / 32);
+//   * it walks 32-token blocks blockIdx.y, += gridDim.y; each block of token rows is
+//     copied once into LDS (direct-to-LDS loads, double-buffered, issued a block ahead)
+//     and read from there by all four waves as the MFMA A operand. LDS row r holds its
+//     16-byte chunk c at c ^ (r % 16), so the fragment reads of 16 rows hit distinct banks;
+//   * a lane's results are channel lane % 32 of tokens 8(r/4) + 4(lane/32) + r%4, so each
+//     store instruction writes two full 128-byte row segments;
+//   * three workgroups per CU, whose stores overlap each other's loads and math.
+constexpr int DT_CH = 128;
+template <int KS>   // K / 16
+__global__ __launch_bounds__(256)
+void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ W,
+                             int64_t ldw, int64_t M, int N, const float* __restrict__ bias,
+                             float* __restrict__ out) {
+  constexpr int K = KS * 16;
+  constexpr int ROWB = K * 2;                 // bytes per token row
+  constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+  constexpr int BLKB = 32 * ROWB;             // bytes per 32-token block
+  constexpr int DPW = BLKB / 1024 / 4;        // 1 KB DMA instructions per wave per block
+  __shared__ __attribute__((aligned(1024))) char sx[2][BLKB];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kh = lane >> 5;
+  const int ch = blockIdx.x * DT_CH + wave * 32 + (lane & 31);
+  bf16x8 w[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    w[s] = *reinterpret_cast<const bf16x8*>(W + (int64_t)ch * ldw + 16 * s + 8 * kh);
+  const float b = bias[ch];
+  // Settle the weight loads here, with a wait the compiler sees (vmcnt(0) = 0x0F70 on gfx9),
+  // so it does not re-wait for them inside the loop, where vmcnt also counts the block
+  // prefetch and the previous block's stores.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  const int64_t nblk = (M + 31) >> 5;
+  // DMA slot of this lane: instruction j of wave w fills LDS bytes [1 KB * (4j + w), +1 KB),
+  // i.e. rows (1024 / ROWB) * (4j + w) + lane / CPR, physical chunk lane % CPR.
+  auto issue = [&](int64_t blk, int buf) {
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int slot = 4 * j + wave;
+      const int r = slot * (1024 / ROWB) + lane / CPR;
+      const int c = (lane % CPR) ^ (r & 15);
+      int64_t t = (blk << 5) + r;
+      if (t >= M) t = M - 1;            // past the end: a copy of the last row, never stored
+      __builtin_amdgcn_global_load_lds((const void*)(X + t * ldx + c * 8),
+                                       (lds_void*)(&sx[buf][slot * 1024]), 16, 0, 0);
+    }
+  };
+  int64_t blk = blockIdx.y;
+  if (blk < nblk) issue(blk, 0);
+  for (int it = 0; blk < nblk; ++it, blk += gridDim.y) {
+    const int buf = it & 1;
+    // this block's rows have landed (the previous block's 16 stores may still be in flight)
+    if (it == 0) wait_vmcnt<0>(); else wait_vmcnt<16>();
+    __builtin_amdgcn_s_barrier();     // ... for every wave; and the other buffer is free
+    if (blk + gridDim.y < nblk) issue(blk + gridDim.y, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const int t0r = lane & 31;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = (2 * s + kh) ^ (t0r & 15);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sx[buf][t0r * ROWB + c * 16]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[s], acc, 0, 0, 0);
+    }
+    const int64_t t0 = blk << 5;
+    float* op = out + (t0 + 4 * kh) * N + ch;
+    if (t0 + 32 <= M) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        op[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = softplus(acc[r] + b);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (t0 + 4 * kh + 8 * (r >> 2) + (r & 3) < M)
+          op[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = softplus(acc[r] + b);
+    }
+  }
+}
+
 template <int EPI>
 hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ldw, int64_t M,
                            int N, int K, const EpiArgs& epi, hipStream_t s) {
+  if (EPI == EPI_SOFTPLUS && (K == 256 || K == 128) && N % DT_CH == 0) {
+    const int64_t nblk = (M + 31) / 32;
+    const dim3 grid(N / DT_CH, (unsigned)(nblk < 32 ? nblk : 32));
+    if (K == 256)
+      hipLaunchKernelGGL(dt_proj_softplus_kernel<16>, grid, dim3(256), 0, s, X, ldx, W, ldw, M, N,
+                         epi.bias, epi.outf0);
+    else
+      hipLaunchKernelGGL(dt_proj_softplus_kernel<8>, grid, dim3(256), 0, s, X, ldx, W, ldw, M, N,
+                         epi.bias, epi.outf0);
+    return hipGetLastError();
+  }
   if (K % MS_BK == 0) {
     const int64_t tiles_m = (M + MS_BM - 1) / MS_BM;
     const int tiles_n = (N + MS_BN - 1) / MS_BN;
@@ -489,6 +588,7 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
                      dim3(256), 0, s, X, ldx, W, ldw, M, N, K, (int)tiles_m, tiles_n, epi);
   return hipGetLastError();
 }
+
 
 template <int EPI>
 hipError_t launch_f32_epi(const float* X, int64_t ldx, const float* W, int64_t ldw, int64_t M,

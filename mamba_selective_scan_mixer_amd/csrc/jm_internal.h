@@ -35,11 +35,12 @@ __device__ __forceinline__ float silu(float v) {
 // log1p(x) for x in [0, 1] with hardware log2: Kahan's identity
 // log1p(x) = x * ln(u) / (u - 1), u = fl(1 + x), which cancels the rounding of
 // 1 + x and keeps a few-ulp relative error even when x is tiny (u == 1 -> x).
+// The quotient uses the hardware reciprocal (about 1 ulp) instead of an IEEE divide.
 __device__ __forceinline__ float log1p_unit(float x) {
   const float u = 1.0f + x;
   const float d = u - 1.0f;
   const float l = __builtin_amdgcn_logf(u) * 0.69314718055994531f;
-  return d == 0.0f ? x : x * (l / d);
+  return d == 0.0f ? x : x * l * __builtin_amdgcn_rcpf(d);
 }
 // softplus(v) = ln(1 + e^v) = max(v, 0) + log1p(e^-|v|): no overflow, and full
 // relative precision for the small step sizes the layer uses (v << 0).

@@ -170,6 +170,58 @@ jm_status jm_prefill_plan(const jm_layer_dims *dims, const int32_t *cu_seqlens_h
  * and for chunk-count invariance tests. Returns JM_ERR_INVALID_ARG if negative. */
 jm_status jm_set_scan_chunk_len(int32_t chunk_len);
 
+/* ---- Stage entry points (diagnostics) -------------------------------------------
+ * Each runs one step of jamba_mamba_prefill on its own, with the same kernels and
+ * launch configuration, so that a step can be checked against a reference fed the
+ * same inputs. The steps are the lines of the per-token recurrence at the top of
+ * this file. T = total_tokens (1 <= T < 2^31); all tensors row-major, T rows;
+ * "act" = act_dtype. Validation and errors as for jamba_mamba_prefill; all weight
+ * pointers must be valid even where a step does not read them.
+ */
+
+/* in_proj: [x ; z] = W_in u.  u (T, d_model) act -> x, z (T, d_inner) act. */
+jm_status jm_stage_in_proj(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                           const void *u, int64_t total_tokens, void *x, void *z, void *stream);
+
+/* Causal depthwise conv (k = d_conv) + SiLU per sequence of cu_seqlens:
+ * x (T, d_inner) act -> x_hat (T, d_inner) act; init_conv_state / final_conv_state
+ * as in jamba_mamba_prefill (both may be NULL). */
+jm_status jm_stage_conv(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                        const void *x, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                        int32_t n_seqs, int64_t total_tokens, const void *init_conv_state,
+                        void *x_hat, void *final_conv_state, void *stream);
+
+/* x_proj: [delta ; B ; C] = W_x x_hat.  x_hat (T, d_inner) act -> delta (T, dt_rank) act,
+ * B and C (T, d_state) fp32. */
+jm_status jm_stage_x_proj(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                          const void *x_hat, int64_t total_tokens, void *delta, float *B,
+                          float *C, void *stream);
+
+/* dt_proj: Delta = softplus(W_dt delta + b_dt).  delta (T, dt_rank) act -> dt (T, d_inner) fp32. */
+jm_status jm_stage_dt_proj(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                           const void *delta, int64_t total_tokens, float *dt, void *stream);
+
+/* Bytes of workspace jm_stage_scan needs (the chunk aggregates of the chunked scan;
+ * 0 when T fits one chunk). */
+jm_status jm_stage_scan_workspace_size(const jm_layer_dims *dims, int64_t total_tokens,
+                                       size_t *bytes);
+
+/* Selective scan with D skip and gate, per sequence of cu_seqlens:
+ *   h_t = exp(Delta_t A) h_{t-1} + Delta_t B_t x_hat_t,  g_t = (C_t . h_t + D x_hat_t) * SiLU(z_t)
+ * x_hat, z (T, d_inner) act; dt (T, d_inner) fp32; B, C (T, d_state) fp32 -> g (T, d_inner)
+ * act. init_ssm_state / final_ssm_state as in jamba_mamba_prefill (may be NULL, must not
+ * overlap). workspace >= jm_stage_scan_workspace_size bytes (may be NULL if that is 0). */
+jm_status jm_stage_scan(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                        const void *x_hat, const float *dt, const float *B, const float *C,
+                        const void *z, const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                        int32_t n_seqs, int64_t total_tokens, const float *init_ssm_state,
+                        void *g, float *final_ssm_state, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* out_proj: out = W_out g.  g (T, d_inner) act -> out (T, d_model) act. */
+jm_status jm_stage_out_proj(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                            const void *g, int64_t total_tokens, void *out, void *stream);
+
 /* ---- Kernel timing (diagnostics; the benchmark reads per-kernel durations) ----
  * While enabled, every kernel the library enqueues is bracketed by a pair of HIP
  * events on the caller's stream. jm_profile_read synchronises those events and

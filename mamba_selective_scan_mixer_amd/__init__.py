@@ -95,9 +95,22 @@ def lib() -> ctypes.CDLL:
         L.jm_profile_reset.argtypes = []
         L.jm_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int32)]
+        D, W = ctypes.POINTER(LayerDims), ctypes.POINTER(LayerWeights)
+        L.jm_stage_in_proj.argtypes = [D, W, _P, ctypes.c_int64, _P, _P, _P]
+        L.jm_stage_conv.argtypes = [D, W, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P,
+                                    _P]
+        L.jm_stage_x_proj.argtypes = [D, W, _P, ctypes.c_int64, _P, _P, _P, _P]
+        L.jm_stage_dt_proj.argtypes = [D, W, _P, ctypes.c_int64, _P, _P]
+        L.jm_stage_scan_workspace_size.argtypes = [D, ctypes.c_int64,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+        L.jm_stage_scan.argtypes = [D, W, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                    ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.jm_stage_out_proj.argtypes = [D, W, _P, ctypes.c_int64, _P, _P]
         for name in ("jm_prefill_workspace_size", "jm_decode_workspace_size", "jamba_mamba_prefill",
                      "jamba_mamba_decode_step", "jm_prefill_plan", "jm_set_scan_chunk_len",
-                     "jm_profile_enable", "jm_profile_reset", "jm_profile_read"):
+                     "jm_profile_enable", "jm_profile_reset", "jm_profile_read",
+                     "jm_stage_in_proj", "jm_stage_conv", "jm_stage_x_proj", "jm_stage_dt_proj",
+                     "jm_stage_scan_workspace_size", "jm_stage_scan", "jm_stage_out_proj"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -289,3 +302,106 @@ def profile_read() -> Dict[str, Tuple[int, float]]:
     arr = (KernelTime * max(n.value, 1))()
     _check(lib().jm_profile_read(arr, n.value, ctypes.byref(n)))
     return {a.name.decode(): (a.launches, a.total_ms) for a in arr[:n.value]}
+
+
+# ---- stage entry points (one step of the prefill each; diagnostics) -----------------------
+
+def jm_stage_in_proj(layer: MambaLayer, u: torch.Tensor, stream=None):
+    """[x ; z] = W_in u; returns (x, z), each (T, d_inner)."""
+    d, dt = layer.dims, _torch_dtype(layer.dims)
+    T = u.shape[0]
+    _need(u, "u", dt, (T, d.d_model))
+    x = torch.empty((T, d.d_inner), dtype=dt, device=u.device)
+    z = torch.empty_like(x)
+    _check(lib().jm_stage_in_proj(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), T,
+                                  _ptr(x), _ptr(z), _stream(stream)))
+    return x, z
+
+
+def jm_stage_conv(layer: MambaLayer, x: torch.Tensor, cu_seqlens: torch.Tensor,
+                  cu_seqlens_host: Sequence[int], init_conv_state=None,
+                  want_final_state: bool = True, stream=None):
+    """Causal conv + SiLU per sequence; returns (x_hat, final_conv_state or None)."""
+    d, dt = layer.dims, _torch_dtype(layer.dims)
+    host, n = _host_cu(cu_seqlens_host)
+    T = host[n]
+    _need(x, "x", dt, (T, d.d_inner))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,))
+    K1 = d.d_conv - 1
+    if init_conv_state is not None:
+        _need(init_conv_state, "init_conv_state", dt, (n, d.d_inner, K1))
+    xh = torch.empty_like(x)
+    fc = torch.empty((n, d.d_inner, K1), dtype=dt, device=x.device) if want_final_state else None
+    _check(lib().jm_stage_conv(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x),
+                               _ptr(cu_seqlens), host, n, T, _ptr(init_conv_state), _ptr(xh),
+                               _ptr(fc), _stream(stream)))
+    return xh, fc
+
+
+def jm_stage_x_proj(layer: MambaLayer, x_hat: torch.Tensor, stream=None):
+    """[delta ; B ; C] = W_x x_hat; returns (delta (T, dt_rank), B (T, N) fp32, C (T, N) fp32)."""
+    d, dt = layer.dims, _torch_dtype(layer.dims)
+    T = x_hat.shape[0]
+    _need(x_hat, "x_hat", dt, (T, d.d_inner))
+    delta = torch.empty((T, d.dt_rank), dtype=dt, device=x_hat.device)
+    B = torch.empty((T, d.d_state), dtype=torch.float32, device=x_hat.device)
+    C = torch.empty_like(B)
+    _check(lib().jm_stage_x_proj(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x_hat), T,
+                                 _ptr(delta), _ptr(B), _ptr(C), _stream(stream)))
+    return delta, B, C
+
+
+def jm_stage_dt_proj(layer: MambaLayer, delta: torch.Tensor, stream=None):
+    """Delta = softplus(W_dt delta + b_dt); returns (T, d_inner) fp32."""
+    d, dt = layer.dims, _torch_dtype(layer.dims)
+    T = delta.shape[0]
+    _need(delta, "delta", dt, (T, d.dt_rank))
+    out = torch.empty((T, d.d_inner), dtype=torch.float32, device=delta.device)
+    _check(lib().jm_stage_dt_proj(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(delta), T,
+                                  _ptr(out), _stream(stream)))
+    return out
+
+
+def jm_stage_scan_workspace_size(dims: LayerDims, total_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jm_stage_scan_workspace_size(ctypes.byref(dims), total_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def jm_stage_scan(layer: MambaLayer, x_hat: torch.Tensor, dt: torch.Tensor, B: torch.Tensor,
+                  C: torch.Tensor, z: torch.Tensor, cu_seqlens: torch.Tensor,
+                  cu_seqlens_host: Sequence[int], init_ssm_state=None,
+                  want_final_state: bool = True, stream=None):
+    """Selective scan + D skip + gate per sequence; returns (g, final_ssm_state or None)."""
+    d, at = layer.dims, _torch_dtype(layer.dims)
+    host, n = _host_cu(cu_seqlens_host)
+    T = host[n]
+    _need(x_hat, "x_hat", at, (T, d.d_inner))
+    _need(z, "z", at, (T, d.d_inner))
+    _need(dt, "dt", torch.float32, (T, d.d_inner))
+    _need(B, "B", torch.float32, (T, d.d_state))
+    _need(C, "C", torch.float32, (T, d.d_state))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,))
+    if init_ssm_state is not None:
+        _need(init_ssm_state, "init_ssm_state", torch.float32, (n, d.d_inner, d.d_state))
+    g = torch.empty_like(x_hat)
+    fs = (torch.empty((n, d.d_inner, d.d_state), dtype=torch.float32, device=x_hat.device)
+          if want_final_state else None)
+    need = jm_stage_scan_workspace_size(d, T)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x_hat.device)
+    _check(lib().jm_stage_scan(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x_hat), _ptr(dt),
+                               _ptr(B), _ptr(C), _ptr(z), _ptr(cu_seqlens), host, n, T,
+                               _ptr(init_ssm_state), _ptr(g), _ptr(fs), _ptr(ws), ws.numel(),
+                               _stream(stream)))
+    return g, fs
+
+
+def jm_stage_out_proj(layer: MambaLayer, g: torch.Tensor, stream=None):
+    """out = W_out g; returns (T, d_model)."""
+    d, dt = layer.dims, _torch_dtype(layer.dims)
+    T = g.shape[0]
+    _need(g, "g", dt, (T, d.d_inner))
+    out = torch.empty((T, d.d_model), dtype=dt, device=g.device)
+    _check(lib().jm_stage_out_proj(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(g), T,
+                                   _ptr(out), _stream(stream)))
+    return out

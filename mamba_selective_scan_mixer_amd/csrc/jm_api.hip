@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -158,8 +159,9 @@ void plan_chunks(const jm_layer_dims& d, int64_t T, int32_t* chunk_len, int32_t*
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct PrefillLayout {
-  size_t x, z, xh, delta, Bm, Cm, dt, aggP, aggh, carry, total;
+  size_t x, z, xh, delta, Bm, Cm, dt, agg, total;
 };
+size_t scan_agg_bytes(const jm_layer_dims& d, int32_t n_chunks);
 
 PrefillLayout prefill_layout(const jm_layer_dims& d, int64_t T, int32_t n_chunks) {
   PrefillLayout L;
@@ -174,10 +176,7 @@ PrefillLayout prefill_layout(const jm_layer_dims& d, int64_t T, int32_t n_chunks
   L.Bm = take(T * 16 * sizeof(float));
   L.Cm = take(T * 16 * sizeof(float));
   L.dt = take(T * di * sizeof(float));
-  const size_t agg = n_chunks > 1 ? (size_t)n_chunks * di * 16 * sizeof(float) : 0;
-  L.aggP = take(agg);
-  L.aggh = take(agg);
-  L.carry = take(agg);
+  L.agg = take(3 * scan_agg_bytes(d, n_chunks));   // decay products | end states | carries
   L.total = off;
   return L;
 }
@@ -221,6 +220,91 @@ EpiArgs epi_none() {
   return e;
 }
 
+// ---- prefill steps (each also exported on its own as a jm_stage_* entry point) -------------
+template <typename T>
+jm_status step_in_proj(const jm_layer_dims& d, const jm_layer_weights& w, const T* u,
+                       int64_t n_tok, T* x, T* z, hipStream_t stream) {
+  EpiArgs e = epi_none();
+  e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = d.d_inner;
+  JM_LAUNCH("in_proj", gemm<T>(u, d.d_model, static_cast<const T*>(w.in_proj_w), d.d_model,
+                               n_tok, 2 * d.d_inner, d.d_model, e, stream));
+  return JM_OK;
+}
+
+template <typename T>
+jm_status step_conv(const jm_layer_dims& d, const jm_layer_weights& w, const T* x,
+                    const int32_t* cu, int32_t n_seqs, int64_t n_tok, const T* init_conv,
+                    T* xh, T* final_conv, hipStream_t stream) {
+  JM_LAUNCH("conv1d_silu",
+            launch_conv_silu<T>(x, xh, static_cast<const T*>(w.conv_w),
+                                static_cast<const T*>(w.conv_b), init_conv, cu, n_seqs, n_tok,
+                                d.d_inner, stream));
+  if (final_conv)
+    JM_LAUNCH("conv_final",
+              launch_conv_final<T>(x, init_conv, final_conv, cu, n_seqs, d.d_inner, stream));
+  return JM_OK;
+}
+
+template <typename T>
+jm_status step_x_proj(const jm_layer_dims& d, const jm_layer_weights& w, const T* xh,
+                      int64_t n_tok, T* delta, float* Bm, float* Cm, hipStream_t stream) {
+  EpiArgs e = epi_none();
+  e.kind = EPI_XPROJ; e.out0 = delta; e.outf0 = Bm; e.outf1 = Cm; e.split = d.dt_rank;
+  e.n_state = 16;
+  JM_LAUNCH("x_proj", gemm<T>(xh, d.d_inner, static_cast<const T*>(w.x_proj_w), d.d_inner, n_tok,
+                              d.dt_rank + 32, d.d_inner, e, stream));
+  return JM_OK;
+}
+
+template <typename T>
+jm_status step_dt_proj(const jm_layer_dims& d, const jm_layer_weights& w, const T* delta,
+                       int64_t n_tok, float* dt, hipStream_t stream) {
+  EpiArgs e = epi_none();
+  e.kind = EPI_SOFTPLUS; e.outf0 = dt; e.bias = w.dt_proj_b;
+  JM_LAUNCH("dt_proj", gemm<T>(delta, d.dt_rank, static_cast<const T*>(w.dt_proj_w), d.dt_rank,
+                               n_tok, d.d_inner, d.dt_rank, e, stream));
+  return JM_OK;
+}
+
+// Scan aggregates (chunk decay products, chunk end states, carries) after the given offset.
+size_t scan_agg_bytes(const jm_layer_dims& d, int32_t n_chunks) {
+  return n_chunks > 1 ? align256((size_t)n_chunks * d.d_inner * 16 * sizeof(float)) : 0;
+}
+
+template <typename T>
+jm_status step_scan(const jm_layer_dims& d, const jm_layer_weights& w, const T* xh,
+                    const float* dt, const float* Bm, const float* Cm, const T* z,
+                    const int32_t* cu, int32_t n_seqs, int64_t n_tok, const float* init_ssm,
+                    T* g, float* final_ssm, char* agg, int32_t chunk_len, int32_t n_chunks,
+                    hipStream_t stream) {
+  const size_t ab = scan_agg_bytes(d, n_chunks);
+  float* aggP = reinterpret_cast<float*>(agg);
+  float* aggh = reinterpret_cast<float*>(agg + ab);
+  float* carry = reinterpret_cast<float*>(agg + 2 * ab);
+  const int di = d.d_inner;
+  if (n_chunks > 1) {
+    JM_LAUNCH("scan_chunk_state",
+              launch_scan_chunk_state<T>(xh, dt, w.A_log, Bm, init_ssm, cu, aggP, aggh, n_seqs,
+                                         n_tok, di, chunk_len, n_chunks - 1, stream));
+    JM_LAUNCH("scan_chunk_carry", launch_scan_chunk_carry(aggP, aggh, carry, di, n_chunks, stream));
+  }
+  JM_LAUNCH("scan_chunk_output",
+            launch_scan_chunk_output<T>(xh, dt, w.A_log, Bm, Cm, w.D, z, g, init_ssm, final_ssm,
+                                        n_chunks > 1 ? carry : nullptr, cu, n_seqs, n_tok, di,
+                                        chunk_len, n_chunks, stream));
+  return JM_OK;
+}
+
+template <typename T>
+jm_status step_out_proj(const jm_layer_dims& d, const jm_layer_weights& w, const T* g,
+                        int64_t n_tok, T* out, hipStream_t stream) {
+  EpiArgs e = epi_none();
+  e.kind = EPI_STORE; e.out0 = out; e.ldo = d.d_model;
+  JM_LAUNCH("out_proj", gemm<T>(g, d.d_inner, static_cast<const T*>(w.out_proj_w), d.d_inner,
+                                n_tok, d.d_model, d.d_inner, e, stream));
+  return JM_OK;
+}
+
 template <typename T>
 jm_status run_prefill(const jm_layer_dims& d, const jm_layer_weights& w, const T* u,
                       const int32_t* cu, int32_t n_seqs, int64_t n_tok, const T* init_conv,
@@ -234,49 +318,17 @@ jm_status run_prefill(const jm_layer_dims& d, const jm_layer_weights& w, const T
   float* Bm = reinterpret_cast<float*>(ws + L.Bm);
   float* Cm = reinterpret_cast<float*>(ws + L.Cm);
   float* dt = reinterpret_cast<float*>(ws + L.dt);
-  float* aggP = reinterpret_cast<float*>(ws + L.aggP);
-  float* aggh = reinterpret_cast<float*>(ws + L.aggh);
-  float* carry = reinterpret_cast<float*>(ws + L.carry);
   T* g = x;  // x is dead once the conv and its final state are done
-  const int di = d.d_inner, dm = d.d_model, R = d.dt_rank;
-  const T* Win = static_cast<const T*>(w.in_proj_w);
-
-  EpiArgs e = epi_none();
-  e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = di;
-  JM_LAUNCH("in_proj", gemm<T>(u, dm, Win, dm, n_tok, 2 * di, dm, e, stream));
-
-  JM_LAUNCH("conv1d_silu",
-            launch_conv_silu<T>(x, xh, static_cast<const T*>(w.conv_w),
-                                static_cast<const T*>(w.conv_b), init_conv, cu, n_seqs, n_tok,
-                                di, stream));
-  if (final_conv)
-    JM_LAUNCH("conv_final", launch_conv_final<T>(x, init_conv, final_conv, cu, n_seqs, di, stream));
-
-  e = epi_none();
-  e.kind = EPI_XPROJ; e.out0 = delta; e.outf0 = Bm; e.outf1 = Cm; e.split = R; e.n_state = 16;
-  JM_LAUNCH("x_proj", gemm<T>(xh, di, static_cast<const T*>(w.x_proj_w), di, n_tok, R + 32, di,
-                              e, stream));
-
-  e = epi_none();
-  e.kind = EPI_SOFTPLUS; e.outf0 = dt; e.bias = w.dt_proj_b;
-  JM_LAUNCH("dt_proj", gemm<T>(delta, R, static_cast<const T*>(w.dt_proj_w), R, n_tok, di, R, e,
-                               stream));
-
-  if (n_chunks > 1) {
-    JM_LAUNCH("scan_chunk_state",
-              launch_scan_chunk_state<T>(xh, dt, w.A_log, Bm, init_ssm, cu, aggP, aggh, n_seqs,
-                                         n_tok, di, chunk_len, n_chunks - 1, stream));
-    JM_LAUNCH("scan_chunk_carry", launch_scan_chunk_carry(aggP, aggh, carry, di, n_chunks, stream));
-  }
-  JM_LAUNCH("scan_chunk_output",
-            launch_scan_chunk_output<T>(xh, dt, w.A_log, Bm, Cm, w.D, z, g, init_ssm, final_ssm,
-                                        n_chunks > 1 ? carry : nullptr, cu, n_seqs, n_tok, di,
-                                        chunk_len, n_chunks, stream));
-
-  e = epi_none();
-  e.kind = EPI_STORE; e.out0 = out; e.ldo = dm;
-  JM_LAUNCH("out_proj", gemm<T>(g, di, static_cast<const T*>(w.out_proj_w), di, n_tok, dm, di, e,
-                                stream));
+  jm_status st;
+  if ((st = step_in_proj<T>(d, w, u, n_tok, x, z, stream)) != JM_OK) return st;
+  if ((st = step_conv<T>(d, w, x, cu, n_seqs, n_tok, init_conv, xh, final_conv, stream)) != JM_OK)
+    return st;
+  if ((st = step_x_proj<T>(d, w, xh, n_tok, delta, Bm, Cm, stream)) != JM_OK) return st;
+  if ((st = step_dt_proj<T>(d, w, delta, n_tok, dt, stream)) != JM_OK) return st;
+  if ((st = step_scan<T>(d, w, xh, dt, Bm, Cm, z, cu, n_seqs, n_tok, init_ssm, g, final_ssm,
+                         ws + L.agg, chunk_len, n_chunks, stream)) != JM_OK)
+    return st;
+  if ((st = step_out_proj<T>(d, w, g, n_tok, out, stream)) != JM_OK) return st;
   return ok();
 }
 
@@ -338,6 +390,31 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
                                     stream));
   return ok();
 }
+
+
+// ---- stage entry points: shared validation ----------------------------------------------
+jm_status check_stage(const jm_layer_dims* dims, const jm_layer_weights* w, int64_t n_tok) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if ((st = check_weights(w)) != JM_OK) return st;
+  if (n_tok < 1 || n_tok >= ((int64_t)1 << 31))
+    return fail(JM_ERR_SHAPE, "total_tokens must be in [1, 2^31) (got %lld)", (long long)n_tok);
+  return JM_OK;
+}
+
+// Required pointers: non-NULL and 16-byte aligned; optional ones: aligned when given.
+jm_status check_ptrs(std::initializer_list<const void*> required,
+                     std::initializer_list<const void*> optional = {}) {
+  for (const void* p : required) {
+    if (!p) return fail(JM_ERR_INVALID_ARG, "a required tensor argument is NULL");
+    if (!aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  }
+  for (const void* p : optional)
+    if (p && !aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  return JM_OK;
+}
+
+bool is_bf16(const jm_layer_dims* d) { return d->act_dtype == JM_BF16; }
 
 }  // namespace
 
@@ -510,6 +587,133 @@ jm_status jamba_mamba_decode_step(const jm_layer_dims* dims, const jm_layer_weig
   return run_decode<float>(*dims, *weights, static_cast<const float*>(u), batch,
                            static_cast<float*>(conv_state), ssm_state, static_cast<float*>(out), ws,
                            s);
+}
+
+// ---- stage entry points ------------------------------------------------------------------
+jm_status jm_stage_in_proj(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                           const void* u, int64_t total_tokens, void* x, void* z, void* stream) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK || (st = check_ptrs({u, x, z})) != JM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = is_bf16(dims) ? step_in_proj<bf16>(*dims, *weights, static_cast<const bf16*>(u),
+                                         total_tokens, static_cast<bf16*>(x),
+                                         static_cast<bf16*>(z), s)
+                     : step_in_proj<float>(*dims, *weights, static_cast<const float*>(u),
+                                           total_tokens, static_cast<float*>(x),
+                                           static_cast<float*>(z), s);
+  return st == JM_OK ? ok() : st;
+}
+
+jm_status jm_stage_conv(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                        const void* x, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                        int32_t n_seqs, int64_t total_tokens, const void* init_conv_state,
+                        void* x_hat, void* final_conv_state, void* stream) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK) return st;
+  if (n_seqs < 1) return fail(JM_ERR_SHAPE, "n_seqs must be >= 1");
+  if (!cu_seqlens) return fail(JM_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if ((st = check_cu(cu_seqlens_host, n_seqs, total_tokens)) != JM_OK) return st;
+  if ((st = check_ptrs({x, x_hat}, {init_conv_state, final_conv_state})) != JM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = is_bf16(dims)
+           ? step_conv<bf16>(*dims, *weights, static_cast<const bf16*>(x), cu_seqlens, n_seqs,
+                             total_tokens, static_cast<const bf16*>(init_conv_state),
+                             static_cast<bf16*>(x_hat), static_cast<bf16*>(final_conv_state), s)
+           : step_conv<float>(*dims, *weights, static_cast<const float*>(x), cu_seqlens, n_seqs,
+                              total_tokens, static_cast<const float*>(init_conv_state),
+                              static_cast<float*>(x_hat), static_cast<float*>(final_conv_state),
+                              s);
+  return st == JM_OK ? ok() : st;
+}
+
+jm_status jm_stage_x_proj(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                          const void* x_hat, int64_t total_tokens, void* delta, float* B,
+                          float* C, void* stream) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK || (st = check_ptrs({x_hat, delta, B, C})) != JM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = is_bf16(dims) ? step_x_proj<bf16>(*dims, *weights, static_cast<const bf16*>(x_hat),
+                                        total_tokens, static_cast<bf16*>(delta), B, C, s)
+                     : step_x_proj<float>(*dims, *weights, static_cast<const float*>(x_hat),
+                                          total_tokens, static_cast<float*>(delta), B, C, s);
+  return st == JM_OK ? ok() : st;
+}
+
+jm_status jm_stage_dt_proj(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                           const void* delta, int64_t total_tokens, float* dt, void* stream) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK || (st = check_ptrs({delta, dt})) != JM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = is_bf16(dims) ? step_dt_proj<bf16>(*dims, *weights, static_cast<const bf16*>(delta),
+                                         total_tokens, dt, s)
+                     : step_dt_proj<float>(*dims, *weights, static_cast<const float*>(delta),
+                                           total_tokens, dt, s);
+  return st == JM_OK ? ok() : st;
+}
+
+jm_status jm_stage_scan_workspace_size(const jm_layer_dims* dims, int64_t total_tokens,
+                                       size_t* bytes) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if (!bytes) return fail(JM_ERR_INVALID_ARG, "bytes is NULL");
+  if (total_tokens < 1 || total_tokens >= ((int64_t)1 << 31))
+    return fail(JM_ERR_SHAPE, "total_tokens must be in [1, 2^31)");
+  int32_t cl, nc;
+  plan_chunks(*dims, total_tokens, &cl, &nc);
+  *bytes = 3 * scan_agg_bytes(*dims, nc);
+  return ok();
+}
+
+jm_status jm_stage_scan(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                        const void* x_hat, const float* dt, const float* B, const float* C,
+                        const void* z, const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                        int32_t n_seqs, int64_t total_tokens, const float* init_ssm_state,
+                        void* g, float* final_ssm_state, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK) return st;
+  if (n_seqs < 1) return fail(JM_ERR_SHAPE, "n_seqs must be >= 1");
+  if (!cu_seqlens) return fail(JM_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if ((st = check_cu(cu_seqlens_host, n_seqs, total_tokens)) != JM_OK) return st;
+  if ((st = check_ptrs({x_hat, dt, B, C, z, g}, {init_ssm_state, final_ssm_state, workspace})) !=
+      JM_OK)
+    return st;
+  if (init_ssm_state && final_ssm_state) {
+    const char* a = reinterpret_cast<const char*>(init_ssm_state);
+    const char* b = reinterpret_cast<const char*>(final_ssm_state);
+    const size_t n = (size_t)n_seqs * dims->d_inner * 16 * sizeof(float);
+    if (a < b + n && b < a + n)
+      return fail(JM_ERR_INVALID_ARG, "init_ssm_state and final_ssm_state must not overlap");
+  }
+  int32_t cl, nc;
+  plan_chunks(*dims, total_tokens, &cl, &nc);
+  const size_t need = 3 * scan_agg_bytes(*dims, nc);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  st = is_bf16(dims)
+           ? step_scan<bf16>(*dims, *weights, static_cast<const bf16*>(x_hat), dt, B, C,
+                             static_cast<const bf16*>(z), cu_seqlens, n_seqs, total_tokens,
+                             init_ssm_state, static_cast<bf16*>(g), final_ssm_state, ws, cl, nc, s)
+           : step_scan<float>(*dims, *weights, static_cast<const float*>(x_hat), dt, B, C,
+                              static_cast<const float*>(z), cu_seqlens, n_seqs, total_tokens,
+                              init_ssm_state, static_cast<float*>(g), final_ssm_state, ws, cl, nc,
+                              s);
+  return st == JM_OK ? ok() : st;
+}
+
+jm_status jm_stage_out_proj(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                            const void* g, int64_t total_tokens, void* out, void* stream) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK || (st = check_ptrs({g, out})) != JM_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = is_bf16(dims) ? step_out_proj<bf16>(*dims, *weights, static_cast<const bf16*>(g),
+                                          total_tokens, static_cast<bf16*>(out), s)
+                     : step_out_proj<float>(*dims, *weights, static_cast<const float*>(g),
+                                            total_tokens, static_cast<float*>(out), s);
+  return st == JM_OK ? ok() : st;
 }
 
 jm_status jm_profile_enable(int32_t enable) {

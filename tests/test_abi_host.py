@@ -159,6 +159,43 @@ def test_decode_validation_paths(L):
     assert call(0, None, None, None, None, None, 0) == S["JM_OK"]
 
 
+def test_stage_validation_paths(L):
+    """Every stage entry point rejects bad arguments on the host (nothing is launched)."""
+    f = _Fake()
+    d = dims()
+    w = _weights(f)
+    S = {n: i for i, n in enumerate(jm._STATUS)}
+    D, W = ctypes.byref(d), ctypes.byref(w)
+    cu = [0, 5, 9]
+    host = (ctypes.c_int32 * 3)(*cu)
+    bad = (ctypes.c_int32 * 3)(0, 5, 5)
+    # in_proj / x_proj / dt_proj / out_proj: null, misaligned, token count
+    assert L.jm_stage_in_proj(D, W, f(), 9, f(), None, None) == S["JM_ERR_INVALID_ARG"]
+    assert L.jm_stage_in_proj(D, W, f() + 4, 9, f(), f(), None) == S["JM_ERR_ALIGNMENT"]
+    assert L.jm_stage_in_proj(D, W, f(), 0, f(), f(), None) == S["JM_ERR_SHAPE"]
+    assert L.jm_stage_x_proj(D, W, f(), 9, f(), f(), None, None) == S["JM_ERR_INVALID_ARG"]
+    assert L.jm_stage_dt_proj(D, W, f(), -1, f(), None) == S["JM_ERR_SHAPE"]
+    assert L.jm_stage_out_proj(D, W, None, 9, f(), None) == S["JM_ERR_INVALID_ARG"]
+    wb = _weights(f, out_proj_w=None)
+    assert L.jm_stage_out_proj(D, ctypes.byref(wb), f(), 9, f(), None) == S["JM_ERR_INVALID_ARG"]
+    # conv: cu_seqlens checks, optional states aligned
+    assert L.jm_stage_conv(D, W, f(), f(), bad, 2, 9, None, f(), None, None) == S["JM_ERR_SHAPE"]
+    assert L.jm_stage_conv(D, W, f(), f(), host, 2, 10, None, f(), None, None) == S["JM_ERR_SHAPE"]
+    assert L.jm_stage_conv(D, W, f(), None, host, 2, 9, None, f(), None, None) == S["JM_ERR_INVALID_ARG"]
+    assert L.jm_stage_conv(D, W, f(), f(), host, 2, 9, f() + 8, f(), None, None) == S["JM_ERR_ALIGNMENT"]
+    # scan: overlap of the two states, workspace size
+    need = ctypes.c_size_t(0)
+    assert L.jm_stage_scan_workspace_size(D, 100000, ctypes.byref(need)) == S["JM_OK"]
+    assert need.value > 0
+    big = (ctypes.c_int32 * 2)(0, 100000)
+    args = lambda st_in, st_out, ws, nb, h=big, n=1, T=100000: (  # noqa: E731
+        D, W, f(), f(), f(), f(), f(), f(), h, n, T, st_in, f(), st_out, ws, nb, None)
+    assert L.jm_stage_scan(*args(None, None, f(), need.value - 1)) == S["JM_ERR_WORKSPACE"]
+    assert L.jm_stage_scan(*args(None, None, None, need.value)) == S["JM_ERR_WORKSPACE"]
+    assert L.jm_stage_scan(*args(0x50000000, 0x50000100, f(), need.value)) == S["JM_ERR_INVALID_ARG"]
+    assert L.jm_stage_scan(*args(None, None, f(), need.value, h=bad, n=2, T=9)) == S["JM_ERR_SHAPE"]
+
+
 def expected_segments(cu, chunk_len):
     """Independent statement of the chunking: chunk c covers [c*L, min((c+1)*L, T))."""
     T = cu[-1]

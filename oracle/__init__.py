@@ -7,5 +7,6 @@ import it. It shares no code with the HIP path (the library under
 """
 from .mamba_ref import (  # noqa: F401
     as_f64, silu, softplus, in_proj, causal_conv_silu, x_proj, dt_proj,
-    selective_scan, gate, out_proj, prefill, decode_step,
+    selective_scan, gate, out_proj, prefill, decode_step, rmsnorm, inner_norm, NORM_KEYS,
+    DEFAULT_NORM_EPS,
 )

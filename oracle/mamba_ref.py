@@ -19,8 +19,11 @@ with these readings (each listed in the design notes):
   * dt = softplus(dt_proj(delta) + dt_bias);
   * A = -exp(A_log); h_t = exp(dt*A) h_{t-1} + dt*B_t*x_t; y_t = C_t.h_t + D*x_t;
   * gate: g = y * SiLU(z); out = out_proj(g); no bias on in/x/out projections;
-  * no inner normalisation (the paper mentions RMSNorm inside the layer in §2 and
-    §6.4 without placing it; it is left out here).
+  * inner normalisation (optional): the paper applies RMSNorm inside the Mamba layer
+    (§2, the paragraph on the Mamba layer's implementation; §6.4 and Fig. 9: added to
+    internal activations after loss spikes at scale) without saying where. When the
+    layer has norm gains, delta, B and C are each RMS-normalised over their own
+    feature axis right after x_proj; without gains the step is absent.
 All arithmetic is fp64 from the exact values of the (bf16 or fp32) inputs, with no
 intermediate rounding. Matrix products use numpy's matmul (a library primitive);
 the recurrence is a plain sequential C loop (scan_ref.c).
@@ -56,11 +59,38 @@ def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
+NORM_KEYS = ("dt_norm_w", "B_norm_w", "C_norm_w")
+DEFAULT_NORM_EPS = 1e-6
+
+
 def as_f64(weights: Dict[str, np.ndarray]) -> Dict[str, np.ndarray]:
     """fp64 copies of the layer parameters (exact: inputs are fp32 or bf16 values)."""
     keys = ("in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b",
             "A_log", "D", "out_proj_w")
-    return {k: _f64(weights[k]) for k in keys}
+    w = {k: _f64(weights[k]) for k in keys}
+    if weights.get("dt_norm_w") is not None:
+        for k in NORM_KEYS:
+            w[k] = _f64(weights[k])
+        w["norm_eps"] = float(weights.get("norm_eps", DEFAULT_NORM_EPS))
+    return w
+
+
+def rmsnorm(v, gain, eps):
+    """Root-mean-square normalisation of each row (the paper's citation [53], Root mean
+    square layer normalization): v / sqrt(mean(v^2) + eps) * gain, over the last axis."""
+    v = _f64(v)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * _f64(gain)
+
+
+def inner_norm(w, delta, B, C):
+    """The layer's inner RMSNorm when it has gains (else the identity): delta, B and C
+    each normalised over its own feature axis, right after x_proj."""
+    if w.get("dt_norm_w") is None:
+        return delta, B, C
+    eps = w.get("norm_eps", DEFAULT_NORM_EPS)
+    return (rmsnorm(delta, w["dt_norm_w"], eps), rmsnorm(B, w["B_norm_w"], eps),
+            rmsnorm(C, w["C_norm_w"], eps))
 
 
 def silu(v):
@@ -150,7 +180,8 @@ def _layer_one_sequence(w, u, conv_hist, h0, keep):
     R = w["dt_proj_w"].shape[1]
     x, z = in_proj(u, w["in_proj_w"], di)
     x_hat, conv_new = causal_conv_silu(x, w["conv_w"], w["conv_b"], conv_hist)
-    delta, B, C = x_proj(x_hat, w["x_proj_w"], R, N)
+    delta_raw, B_raw, C_raw = x_proj(x_hat, w["x_proj_w"], R, N)
+    delta, B, C = inner_norm(w, delta_raw, B_raw, C_raw)
     dt = dt_proj(delta, w["dt_proj_w"], w["dt_proj_b"])
     A = -np.exp(w["A_log"])
     y, h_last = selective_scan(x_hat, dt, A, B, C, w["D"], h0)
@@ -158,7 +189,8 @@ def _layer_one_sequence(w, u, conv_hist, h0, keep):
     out = out_proj(g, w["out_proj_w"])
     stages = None
     if keep:
-        stages = dict(x=x, z=z, x_hat=x_hat, delta=delta, B=B, C=C, dt=dt, y=y, g=g)
+        stages = dict(x=x, z=z, x_hat=x_hat, delta_raw=delta_raw, B_raw=B_raw, C_raw=C_raw,
+                      delta=delta, B=B, C=C, dt=dt, y=y, g=g)
     return out, conv_new, h_last, stages
 
 
@@ -215,6 +247,11 @@ def decode_step(weights, u, conv_state, ssm_state):
     x_hat = conv / (1.0 + np.exp(-conv))
     dbc = x_hat @ w["x_proj_w"].T
     delta, Bm, Cm = dbc[:, :R], dbc[:, R:R + N], dbc[:, R + N:]
+    if w.get("dt_norm_w") is not None:      # inner RMSNorm of delta, B and C
+        e = w.get("norm_eps", DEFAULT_NORM_EPS)
+        delta = delta * w["dt_norm_w"][None, :] / np.sqrt((delta ** 2).mean(axis=1)[:, None] + e)
+        Bm = Bm * w["B_norm_w"][None, :] / np.sqrt((Bm ** 2).mean(axis=1)[:, None] + e)
+        Cm = Cm * w["C_norm_w"][None, :] / np.sqrt((Cm ** 2).mean(axis=1)[:, None] + e)
     pre = delta @ w["dt_proj_w"].T + w["dt_proj_b"][None, :]
     dt = np.maximum(pre, 0.0) + np.log1p(np.exp(-np.abs(pre)))
     A = -np.exp(w["A_log"])                         # (di, N)

@@ -22,7 +22,8 @@ dt bias = inverse softplus of dt0, dt0 log-uniform in [1e-3, 1e-1]; inputs N(0, 
 Random stream: numpy PCG64 seeded per workload; draws are fp64, cast to fp32,
 then rounded to bf16 for bf16 workloads. Fixed draw order:
 [packed lengths] -> in_proj -> conv_w -> conv_b -> x_proj -> dt_proj -> U(dt) ->
-out_proj -> inputs (decode: prefill tokens, then each step's tokens in order).
+out_proj -> [inner-norm gains: delta, B, C] -> inputs (decode: prefill tokens, then each
+step's tokens in order).
 """
 from __future__ import annotations
 
@@ -110,8 +111,12 @@ def _normal(rng: np.random.Generator, shape, dtype: str, std: float = 1.0,
     return out
 
 
+NORM_GAIN_STD = 0.1
+NORM_EPS = 1e-6
+
+
 def make_weights(dims: LayerDims, dtype: str, rng: np.random.Generator,
-                 D_value: float = 1.0) -> Dict[str, np.ndarray]:
+                 D_value: float = 1.0, inner_norm: bool = False) -> Dict[str, np.ndarray]:
     """Layer parameters, drawn in the fixed order documented in the module docstring.
 
     Layouts (row-major): in_proj_w (2*d_inner, d_model) with x rows first, then z;
@@ -121,6 +126,10 @@ def make_weights(dims: LayerDims, dtype: str, rng: np.random.Generator,
     D (d_inner) fp32; out_proj_w (d_model, d_inner).
     Weight matrices are fp32 arrays holding `dtype` values; A_log, D and dt_proj_b
     are fp32 in every workload (they parameterise the fp32 recurrence).
+    With inner_norm, three fp32 RMSNorm gain vectors follow, drawn after out_proj_w
+    (so every other parameter is the same as without): dt_norm_w (dt_rank), B_norm_w and
+    C_norm_w (d_state), each 1 + N(0, 0.1^2) so that a dropped gain is visible, and
+    norm_eps = 1e-6.
     """
     di, dm, N, K, R = dims.d_inner, dims.d_model, dims.d_state, dims.d_conv, dims.dt_rank
     w = {}
@@ -133,6 +142,10 @@ def make_weights(dims: LayerDims, dtype: str, rng: np.random.Generator,
     dt0 = np.exp(np.log(DT_MIN) + U * (np.log(DT_MAX) - np.log(DT_MIN)))
     w["dt_proj_b"] = np.log(np.expm1(dt0)).astype(np.float32)   # softplus^{-1}(dt0)
     w["out_proj_w"] = _normal(rng, (dm, di), dtype, WEIGHT_STD)
+    if inner_norm:
+        for k, n in (("dt_norm_w", R), ("B_norm_w", N), ("C_norm_w", N)):
+            w[k] = (1.0 + NORM_GAIN_STD * rng.standard_normal(n)).astype(np.float32)
+        w["norm_eps"] = NORM_EPS
     w["A_log"] = np.tile(np.log(np.arange(1, N + 1, dtype=np.float64)), (di, 1)).astype(np.float32)
     w["D"] = np.full(di, D_value, dtype=np.float32)
     w["dt0"] = dt0   # fp64, kept for the softplus round-trip pin (not a layer weight)
@@ -172,7 +185,7 @@ def make_workload(name: str, seed: int = 0, D_value: float = 1.0, *,
                   lengths: Optional[List[int]] = None, n_seqs: Optional[int] = None,
                   batch: Optional[int] = None, prefill_len: Optional[int] = None,
                   steps: Optional[int] = None, dims: Optional[LayerDims] = None,
-                  dtype: Optional[str] = None) -> Workload:
+                  dtype: Optional[str] = None, inner_norm: bool = False) -> Workload:
     """Build a named workload; keyword overrides give scaled-down variants for tests.
 
     Overrides keep the draw order, so e.g. a packed workload with n_seqs=3 draws
@@ -195,7 +208,7 @@ def make_workload(name: str, seed: int = 0, D_value: float = 1.0, *,
     elif lengths is None:
         lengths = list(spec["lengths"])
     lengths = [int(v) for v in lengths]
-    w = make_weights(dims, dtype, rng, D_value)
+    w = make_weights(dims, dtype, rng, D_value, inner_norm)
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
     u = _normal(rng, (int(cu[-1]), dims.d_model), dtype)

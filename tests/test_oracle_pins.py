@@ -90,6 +90,18 @@ def brute_layer(w, u, conv_hist=None, h0=None):
     dbc = np.array([[sum(float(W_x[r, d]) * xh[t, d] for d in range(di)) for r in range(R + 2 * N)]
                     for t in range(T)])
     delta, Bm, Cm = dbc[:, :R], dbc[:, R:R + N], dbc[:, R + N:]
+    if w.get("dt_norm_w") is not None:   # inner RMSNorm, row by row in plain loops
+        eps = float(w.get("norm_eps", 1e-6))
+
+        def rms_rows(M, gain):
+            out_rows = []
+            for row in M:
+                r = math.sqrt(sum(float(v) * float(v) for v in row) / len(row) + eps)
+                out_rows.append([float(v) / r * float(g) for v, g in zip(row, gain)])
+            return np.array(out_rows)
+
+        delta, Bm, Cm = (rms_rows(delta, w["dt_norm_w"]), rms_rows(Bm, w["B_norm_w"]),
+                         rms_rows(Cm, w["C_norm_w"]))
     dt = np.zeros((T, di))
     for t in range(T):
         for d in range(di):
@@ -119,6 +131,18 @@ def tiny_weights(rng, dm=4, di=4, N=3, K=4, R=2, D_value=1.0, scale=0.5):
         "D": np.full(di, D_value),
         "out_proj_w": rng.standard_normal((dm, di)) * scale,
     }
+    return w
+
+
+def with_norm(w, rng, eps=1e-6):
+    """The same tiny layer with inner-RMSNorm gains (not close to 1, so they matter)."""
+    w = dict(w)
+    R = w["dt_proj_w"].shape[1]
+    N = w["A_log"].shape[1]
+    w["dt_norm_w"] = 1.0 + 0.5 * rng.standard_normal(R)
+    w["B_norm_w"] = 1.0 + 0.5 * rng.standard_normal(N)
+    w["C_norm_w"] = 1.0 + 0.5 * rng.standard_normal(N)
+    w["norm_eps"] = eps
     return w
 
 
@@ -354,6 +378,62 @@ def check_layer_bruteforce():
         assert rel_err(r["out"], ob) < 1e-11 and rel_err(r["conv_state"][0], cb_) < TOL
 
 
+def check_rmsnorm_closed_form():
+    # v / sqrt(mean(v^2) + eps) * gain on hand values
+    s = math.sqrt(12.5)
+    assert np.allclose(oracle.rmsnorm([[3.0, 4.0]], [1.0, 1.0], 0.0), [[3 / s, 4 / s]], rtol=0, atol=1e-15)
+    assert np.allclose(oracle.rmsnorm([[3.0, 4.0]], [2.0, -1.0], 0.0), [[6 / s, -4 / s]], rtol=0, atol=1e-15)
+    # eps sits inside the root, added to the mean square: 1e-3 / sqrt(1e-6 + 1e-6) = 1/sqrt(2)
+    assert abs(oracle.rmsnorm([[1e-3]], [1.0], 1e-6)[0, 0] - 1 / math.sqrt(2)) < 1e-15
+    # a mean, not a sum; rows are independent; an all-zero row stays zero
+    r = oracle.rmsnorm([[1.0, 1.0, 1.0, 1.0], [0.0, 0.0, 0.0, 0.0]], [1.0] * 4, 1e-6)
+    assert abs(r[0, 0] - 1 / math.sqrt(1 + 1e-6)) < 1e-15 and np.all(r[1] == 0.0)
+
+
+def check_rmsnorm_invariants():
+    rng = np.random.default_rng(21)
+    v = rng.standard_normal((5, 256))
+    g = np.ones(256)
+    r = oracle.rmsnorm(v, g, 0.0)
+    assert rel_err(oracle.rmsnorm(7.3 * v, g, 0.0), r) < TOL          # scale invariance
+    assert np.max(np.abs(np.mean(r * r, axis=1) - 1.0)) < TOL          # unit mean square
+
+
+def check_layer_bruteforce_inner_norm():
+    rng = np.random.default_rng(22)
+    for D_value in (1.0, 0.0):
+        w_plain = tiny_weights(rng, D_value=D_value)
+        w = with_norm(w_plain, rng)
+        T = 6
+        u = rng.standard_normal((T, 4))
+        hist = rng.standard_normal((4, 3))
+        h0 = rng.standard_normal((4, 3)) * 0.3
+        r = oracle.prefill(w, u, [0, T], init_conv=hist[None], init_ssm=h0[None])
+        ob, cb_, hb = brute_layer(w, u, hist, h0)
+        assert rel_err(r["out"], ob) < 1e-11
+        assert rel_err(r["ssm_state"][0], hb) < 1e-11
+        # the norm changes the result (the step is not a no-op on this layer)
+        plain = oracle.prefill(w_plain, u, [0, T], init_conv=hist[None], init_ssm=h0[None])
+        assert rel_err(r["out"], plain["out"]) > 1e-3
+
+
+def check_prefill_vs_decode_inner_norm():
+    """The decode step (its own code) agrees with the prefill when the norm is on."""
+    rng = np.random.default_rng(23)
+    w = with_norm(tiny_weights(rng), rng)
+    T = 7
+    u = rng.standard_normal((T, 4))
+    r = oracle.prefill(w, u, [0, T])
+    conv = np.zeros((1, 4, 3))
+    ssm = np.zeros((1, 4, 3))
+    outs = []
+    for t in range(T):
+        o, conv, ssm = oracle.decode_step(w, u[t:t + 1], conv, ssm)
+        outs.append(o[0])
+    assert rel_err(np.array(outs), r["out"]) < 1e-12
+    assert rel_err(ssm, r["ssm_state"]) < 1e-12
+
+
 PINS = {
     "scan_bruteforce": check_scan_bruteforce,
     "scan_geometric": check_scan_geometric,
@@ -366,6 +446,10 @@ PINS = {
     "linearity": check_linearity,
     "small_integer_stages": check_small_integer_stages,
     "layer_bruteforce": check_layer_bruteforce,
+    "rmsnorm_closed_form": check_rmsnorm_closed_form,
+    "rmsnorm_invariants": check_rmsnorm_invariants,
+    "layer_bruteforce_inner_norm": check_layer_bruteforce_inner_norm,
+    "prefill_vs_decode_inner_norm": check_prefill_vs_decode_inner_norm,
 }
 
 
@@ -421,8 +505,27 @@ def _mut_scan_ignores_h0(x, dt, A, B, C, D, h0=None):
     return _orig["selective_scan"](x, dt, A, B, C, D, None)
 
 
+def _mut_rms_eps_outside(v, gain, eps):
+    v = np.asarray(v, dtype=np.float64)
+    return v / (np.sqrt(np.mean(v * v, axis=-1, keepdims=True)) + eps) * np.asarray(gain)
+
+
+def _mut_rms_sum(v, gain, eps):
+    v = np.asarray(v, dtype=np.float64)
+    return v / np.sqrt(np.sum(v * v, axis=-1, keepdims=True) + eps) * np.asarray(gain)
+
+
+def _mut_rms_no_gain(v, gain, eps):
+    return _orig["rmsnorm"](v, np.ones_like(np.asarray(gain, dtype=np.float64)), eps)
+
+
+def _mut_inner_norm_skips_B(w, delta, B, C):
+    d, _, c = _orig["inner_norm"](w, delta, B, C)
+    return d, B, c
+
+
 _orig = {k: getattr(ref, k) for k in ("causal_conv_silu", "in_proj", "softplus", "silu", "gate",
-                                      "x_proj", "selective_scan")}
+                                      "x_proj", "selective_scan", "rmsnorm", "inner_norm")}
 
 MUTATIONS = [
     ("causal_conv_silu", _mut_conv_reversed),
@@ -433,6 +536,10 @@ MUTATIONS = [
     ("selective_scan", _mut_scan_no_skip),
     ("selective_scan", _mut_scan_sign),
     ("selective_scan", _mut_scan_ignores_h0),
+    ("rmsnorm", _mut_rms_eps_outside),
+    ("rmsnorm", _mut_rms_sum),
+    ("rmsnorm", _mut_rms_no_gain),
+    ("inner_norm", _mut_inner_norm_skips_B),
 ]
 
 

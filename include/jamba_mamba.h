@@ -80,6 +80,16 @@ typedef struct {
     const float *A_log;       /* (d_inner, d_state) fp32; A = -exp(A_log)                      */
     const float *D;           /* (d_inner) fp32 skip weight                                    */
     const void  *out_proj_w;  /* (d_model, d_inner)                                            */
+    /* Optional inner RMSNorm (Jamba paper §2, the paragraph on the Mamba layer's
+     * implementation, and §6.4 / Fig. 9: RMSNorm on the layer's internal activations,
+     * placement not given). Here: right after x_proj, delta, B and C are each replaced
+     * by v / sqrt(mean(v^2) + norm_eps) * gain over their own feature axis (fp32 math),
+     * before dt_proj and the scan. All three gains NULL: no norm (the plain layer).
+     * All three set: norm on, and norm_eps must be finite and > 0. Mixed: rejected. */
+    const float *dt_norm_w;   /* (dt_rank) fp32 or NULL                                        */
+    const float *B_norm_w;    /* (d_state) fp32 or NULL                                        */
+    const float *C_norm_w;    /* (d_state) fp32 or NULL                                        */
+    float        norm_eps;
 } jm_layer_weights;
 
 /* Human-readable name of a status. Never NULL. */

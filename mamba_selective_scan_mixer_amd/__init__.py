@@ -39,7 +39,7 @@ class LayerDims(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D",
-        "out_proj_w")]
+        "out_proj_w", "dt_norm_w", "B_norm_w", "C_norm_w")] + [("norm_eps", ctypes.c_float)]
 
 
 class ChunkSegment(ctypes.Structure):
@@ -136,20 +136,27 @@ class MambaLayer:
 
     WEIGHT_KEYS = ("in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b",
                    "A_log", "D", "out_proj_w")
-    FP32_KEYS = ("dt_proj_b", "A_log", "D")
+    NORM_KEYS = ("dt_norm_w", "B_norm_w", "C_norm_w")     # optional inner RMSNorm gains
+    FP32_KEYS = ("dt_proj_b", "A_log", "D") + NORM_KEYS
+    DEFAULT_NORM_EPS = 1e-6
 
-    def __init__(self, dims: LayerDims, tensors: Dict[str, torch.Tensor]):
+    def __init__(self, dims: LayerDims, tensors: Dict[str, torch.Tensor],
+                 norm_eps: Optional[float] = None):
         self.dims = dims
         dt = _torch_dtype(dims)
         di, dm, N, K, R = dims.d_inner, dims.d_model, dims.d_state, dims.d_conv, dims.dt_rank
         shapes = {"in_proj_w": (2 * di, dm), "conv_w": (di, K), "conv_b": (di,),
                   "x_proj_w": (R + 2 * N, di), "dt_proj_w": (di, R), "dt_proj_b": (di,),
-                  "A_log": (di, N), "D": (di,), "out_proj_w": (dm, di)}
+                  "A_log": (di, N), "D": (di,), "out_proj_w": (dm, di),
+                  "dt_norm_w": (R,), "B_norm_w": (N,), "C_norm_w": (N,)}
         self.tensors: Dict[str, Optional[torch.Tensor]] = {}
-        for k in self.WEIGHT_KEYS:
+        has_norm = [tensors.get(k) is not None for k in self.NORM_KEYS]
+        if any(has_norm) and not all(has_norm):
+            raise ValueError("inner norm: give all of dt_norm_w, B_norm_w, C_norm_w or none")
+        for k in self.WEIGHT_KEYS + self.NORM_KEYS:
             t = tensors.get(k)
             if t is None:
-                if k == "conv_b":
+                if k == "conv_b" or k in self.NORM_KEYS:
                     self.tensors[k] = None
                     continue
                 raise ValueError(f"missing weight {k}")
@@ -158,20 +165,24 @@ class MambaLayer:
                 raise ValueError(f"{k}: need contiguous {want} {shapes[k]} on the GPU, got "
                                  f"{t.dtype} {tuple(t.shape)} on {t.device}")
             self.tensors[k] = t
+        self.inner_norm = all(has_norm)
+        self.norm_eps = float(self.DEFAULT_NORM_EPS if norm_eps is None else norm_eps)
         self.struct = LayerWeights(*[(self.tensors[k].data_ptr() if self.tensors[k] is not None
-                                      else None) for k in self.WEIGHT_KEYS])
+                                      else None) for k in self.WEIGHT_KEYS + self.NORM_KEYS],
+                                   self.norm_eps if self.inner_norm else 0.0)
 
     @classmethod
     def from_arrays(cls, dims: LayerDims, arrays: Dict[str, "object"], device="cuda") -> "MambaLayer":
         """Copy host arrays (numpy or torch) to the device in the layer's dtypes."""
         dt = _torch_dtype(dims)
         ts = {}
-        for k in cls.WEIGHT_KEYS:
+        for k in cls.WEIGHT_KEYS + cls.NORM_KEYS:
             if k not in arrays or arrays[k] is None:
                 continue
             a = torch.as_tensor(arrays[k])
             ts[k] = a.to(device=device, dtype=torch.float32 if k in cls.FP32_KEYS else dt).contiguous()
-        return cls(dims, ts)
+        eps = arrays.get("norm_eps") if hasattr(arrays, "get") else None
+        return cls(dims, ts, None if eps is None else float(eps))
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -119,6 +119,16 @@ jm_status check_weights(const jm_layer_weights* w) {
   }
   if (w->conv_b && !aligned16(w->conv_b))
     return fail(JM_ERR_ALIGNMENT, "weights->conv_b not 16-byte aligned");
+  const int n_gains = (w->dt_norm_w != nullptr) + (w->B_norm_w != nullptr) + (w->C_norm_w != nullptr);
+  if (n_gains != 0 && n_gains != 3)
+    return fail(JM_ERR_INVALID_ARG, "inner norm: dt_norm_w, B_norm_w and C_norm_w must be all "
+                "set or all NULL");
+  if (n_gains == 3) {
+    if (!(w->norm_eps > 0.0f) || !(w->norm_eps < 3.0e38f))
+      return fail(JM_ERR_INVALID_ARG, "inner norm: norm_eps must be finite and > 0");
+    if (!aligned16(w->dt_norm_w) || !aligned16(w->B_norm_w) || !aligned16(w->C_norm_w))
+      return fail(JM_ERR_ALIGNMENT, "inner norm gains must be 16-byte aligned");
+  }
   return JM_OK;
 }
 
@@ -253,6 +263,10 @@ jm_status step_x_proj(const jm_layer_dims& d, const jm_layer_weights& w, const T
   e.n_state = 16;
   JM_LAUNCH("x_proj", gemm<T>(xh, d.d_inner, static_cast<const T*>(w.x_proj_w), d.d_inner, n_tok,
                               d.dt_rank + 32, d.d_inner, e, stream));
+  if (w.dt_norm_w)
+    JM_LAUNCH("inner_norm", launch_inner_rmsnorm<T>(delta, Bm, Cm, w.dt_norm_w, w.B_norm_w,
+                                                    w.C_norm_w, w.norm_eps, n_tok, d.dt_rank,
+                                                    stream));
   return JM_OK;
 }
 
@@ -360,6 +374,10 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
                                                     M, dm, di, stream));
         JM_LAUNCH("dec_x_proj", launch_dec_x_proj(xh, static_cast<const bf16*>(w.x_proj_w),
                                                   partial, delta, Bm, Cm, M, di, R, stream));
+        if (w.dt_norm_w)
+          JM_LAUNCH("dec_inner_norm",
+                    launch_inner_rmsnorm<bf16>(delta, Bm, Cm, w.dt_norm_w, w.B_norm_w, w.C_norm_w,
+                                               w.norm_eps, M, R, stream));
         JM_LAUNCH("dec_update", launch_dec_update(xh, z, delta, Bm, Cm,
                                                   static_cast<const bf16*>(w.dt_proj_w),
                                                   w.dt_proj_b, w.A_log, w.D, st, g, M, di, R,
@@ -381,6 +399,9 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
   e.kind = EPI_XPROJ; e.out0 = delta; e.outf0 = Bm; e.outf1 = Cm; e.split = R; e.n_state = 16;
   JM_LAUNCH("dec_x_proj", gemm<T>(xh, di, static_cast<const T*>(w.x_proj_w), di, b, R + 32, di, e,
                                   stream));
+  if (w.dt_norm_w)
+    JM_LAUNCH("dec_inner_norm", launch_inner_rmsnorm<T>(delta, Bm, Cm, w.dt_norm_w, w.B_norm_w,
+                                                        w.C_norm_w, w.norm_eps, b, R, stream));
   JM_LAUNCH("dec_update",
             launch_decode_update<T>(xh, z, delta, Bm, Cm, static_cast<const T*>(w.dt_proj_w),
                                     w.dt_proj_b, w.A_log, w.D, ssm_state, g, b, di, R, stream));

@@ -110,6 +110,13 @@ hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const f
                                 const float* A_log, const float* D, float* ssm_state, T* g,
                                 int batch, int d_inner, int dt_rank, hipStream_t s);
 
+// Inner RMSNorm (optional), in place, row by row: delta (M, R) act dtype, B and C (M, 16)
+// fp32, each v <- v / sqrt(mean(v^2) + eps) * gain.
+template <typename T>
+hipError_t launch_inner_rmsnorm(T* delta, float* Bm, float* Cm, const float* g_delta,
+                                const float* g_B, const float* g_C, float eps, int64_t M, int R,
+                                hipStream_t s);
+
 // Decode fast path (bf16; d_model % 256, d_inner % 1024, dt_rank % 128; <= 64 rows per launch).
 bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank);
 size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile);

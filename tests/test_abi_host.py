@@ -142,6 +142,15 @@ def test_prefill_validation_paths(L):
     assert _prefill(L, d, w, [0, 5], fake=f, u=1, init_conv=0x40000008) == S["JM_ERR_ALIGNMENT"]
     # empty input: no sequences, no tokens -> nothing to do
     assert _prefill(L, d, w, [0], fake=f, u=0, out=0, ws=0) == S["JM_OK"]
+    # inner norm: all three gains or none; eps finite and > 0; gains aligned
+    wn = _weights(f, dt_norm_w=f(), B_norm_w=f(), C_norm_w=None, norm_eps=1e-6)
+    assert _prefill(L, d, wn, [0, 5], fake=f) == S["JM_ERR_INVALID_ARG"]
+    assert "all" in L.jm_last_error().decode()
+    for eps in (0.0, -1.0, float("inf"), float("nan")):
+        we = _weights(f, dt_norm_w=f(), B_norm_w=f(), C_norm_w=f(), norm_eps=eps)
+        assert _prefill(L, d, we, [0, 5], fake=f) == S["JM_ERR_INVALID_ARG"], eps
+    wa = _weights(f, dt_norm_w=f(), B_norm_w=f() + 4, C_norm_w=f(), norm_eps=1e-6)
+    assert _prefill(L, d, wa, [0, 5], fake=f) == S["JM_ERR_ALIGNMENT"]
 
 
 def test_decode_validation_paths(L):

@@ -97,12 +97,13 @@ def cpu_baseline(wl, target_s: float = 15.0):
         blas_threads = os.cpu_count() or 1
     omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     w64 = oracle.as_f64(wl.weights)
-    # calibrate on a small sample, then size the timed sample for ~target_s
-    n0 = 64
+    # calibrate on a small sample, then size the timed sample for ~target_s (at most 48K
+    # tokens: the fp64 intermediates take ~0.5 MB per token)
+    n0 = 512
     t = time.perf_counter()
     oracle.prefill(w64, wl.u[:n0], [0, n0])
     dt0 = time.perf_counter() - t
-    n = int(min(4096, max(n0, n0 * target_s / max(dt0, 1e-3))))
+    n = int(min(49152, max(n0, n0 * target_s / max(dt0, 1e-3))))
     t = time.perf_counter()
     oracle.prefill(w64, wl.u[:n], [0, n])
     el = time.perf_counter() - t
@@ -119,6 +120,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-inner-norm", action="store_true",
+                    help="skip the prefill measurement with the inner RMSNorm on")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
@@ -215,6 +218,12 @@ def main():
             roof = {"kernel": dom, "bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": kd["frac"], "traffic": None}
 
+    inner = None
+    if not args.no_inner_norm:
+        inner = run_inner_norm(jm, torch, wl, dims, u, cu, out, fconv, fssm, ws, T)
+        print(f"[bench] prefill with inner norm {inner['ms_per_step']:.2f} ms/step "
+              f"(norm kernel {inner['norm_kernel']['avg_ms']:.3f} ms)", file=sys.stderr, flush=True)
+
     decode = None
     if not args.no_decode:
         decode = run_decode(jm, torch, dev, layer, dims, wl, args.decode_steps)
@@ -239,9 +248,48 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "decode": decode,
+        "inner_norm": inner,
         "kernels": kernels,
     }
     print(json.dumps(rec), flush=True)
+
+
+def run_inner_norm(jm, torch, wl, dims, u, cu, out, fconv, fssm, ws, T, steps: int = 5):
+    """The same prefill with the optional inner RMSNorm on (synthetic gains, seed 1)."""
+    import synth
+    gains = synth.make_norm_gains(wl.dims, np.random.default_rng(1))
+    arrays = dict(wl.weights)
+    arrays.update(gains)
+    layer = jm.MambaLayer.from_arrays(dims, arrays)
+
+    def step():
+        jm.jamba_mamba_prefill(layer, u, cu, wl.cu_seqlens, out=out, final_conv_state=fconv,
+                               final_ssm_state=fssm, workspace=ws)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    jm.profile_reset()
+    jm.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    jm.profile_enable(False)
+    prof = jm.profile_read()
+    jm.profile_reset()
+    n, ms = prof.get("inner_norm", (0, 0.0))
+    avg = ms / max(n, 1)
+    R, N = wl.dims.dt_rank, wl.dims.d_state
+    nbytes = T * (2 * R * 2 + 2 * 2 * N * 4)      # delta bf16, B and C fp32: read + write
+    return {"ms_per_step": round(el * 1e3 / steps, 3), "tokens_per_s": round(T * steps / el, 1),
+            "steps": steps,
+            "placement": "RMSNorm of delta, B and C right after x_proj (gains 1 + N(0, 0.01))",
+            "norm_kernel": {"avg_ms": round(avg, 4), "bytes": nbytes,
+                            "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1) if avg else None,
+                            "bound": "hbm",
+                            "frac": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if avg else None}}
 
 
 def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
@@ -286,6 +334,19 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
         graph.replay()
     torch.cuda.synchronize()
     el = (time.perf_counter() - t0) * steps / (reps * G)
+    # cold: a 1 GiB read before each timed step evicts weights and state from the 256 MB
+    # Infinity Cache; events bracket the step only
+    scrub = torch.ones(2**28, dtype=torch.float32, device=dev)
+    cold = []
+    for s in range(min(32, steps)):
+        _ = scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
+        e1.record()
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del scrub
     # per-kernel breakdown in a separate eager pass (events between kernels perturb short steps)
     jm.profile_reset()
     jm.profile_enable(True)
@@ -302,6 +363,9 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
     return {"batch": B, "context": L0, "steps": steps, "us_per_step": el * 1e6 / steps,
             "tokens_per_s": B * steps / el, "timing": "HIP graph of 16 steps, replayed",
             "us_per_step_eager": el_eager * 1e6 / steps,
+            "us_per_step_cold": round(float(np.median(cold)), 2),
+            "cold_note": "median of 32 single steps, each after a 1 GiB read (Infinity Cache "
+                         "flushed), HIP events around the step",
             "algorithmic_bytes_per_step": per_step,
             "hbm_frac": per_step / (el / steps) / 1e9 / HBM_PEAK_GBS,
             "kernels_us": {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in prof.items()}}

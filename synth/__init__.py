@@ -115,6 +115,17 @@ NORM_GAIN_STD = 0.1
 NORM_EPS = 1e-6
 
 
+def make_norm_gains(dims: LayerDims, rng: np.random.Generator) -> Dict[str, np.ndarray]:
+    """Inner-RMSNorm gains (fp32): delta (dt_rank), B and C (d_state), each 1 + N(0, 0.1^2),
+    drawn in that order; plus norm_eps."""
+    g = {}
+    for k, n in (("dt_norm_w", dims.dt_rank), ("B_norm_w", dims.d_state),
+                 ("C_norm_w", dims.d_state)):
+        g[k] = (1.0 + NORM_GAIN_STD * rng.standard_normal(n)).astype(np.float32)
+    g["norm_eps"] = NORM_EPS
+    return g
+
+
 def make_weights(dims: LayerDims, dtype: str, rng: np.random.Generator,
                  D_value: float = 1.0, inner_norm: bool = False) -> Dict[str, np.ndarray]:
     """Layer parameters, drawn in the fixed order documented in the module docstring.
@@ -143,9 +154,7 @@ def make_weights(dims: LayerDims, dtype: str, rng: np.random.Generator,
     w["dt_proj_b"] = np.log(np.expm1(dt0)).astype(np.float32)   # softplus^{-1}(dt0)
     w["out_proj_w"] = _normal(rng, (dm, di), dtype, WEIGHT_STD)
     if inner_norm:
-        for k, n in (("dt_norm_w", R), ("B_norm_w", N), ("C_norm_w", N)):
-            w[k] = (1.0 + NORM_GAIN_STD * rng.standard_normal(n)).astype(np.float32)
-        w["norm_eps"] = NORM_EPS
+        w.update(make_norm_gains(dims, rng))
     w["A_log"] = np.tile(np.log(np.arange(1, N + 1, dtype=np.float64)), (di, 1)).astype(np.float32)
     w["D"] = np.full(di, D_value, dtype=np.float32)
     w["dt0"] = dt0   # fp64, kept for the softplus round-trip pin (not a layer weight)

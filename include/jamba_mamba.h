@@ -153,6 +153,51 @@ jm_status jamba_mamba_decode_step(const jm_layer_dims *dims, const jm_layer_weig
                                   float *ssm_state, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* ---- State cache (serving) ------------------------------------------------------------
+ * The per-sequence state is what replaces the KV cache (Jamba paper §2, the KV-cache
+ * paragraph and Table 1; §3.1: long contexts on one 80 GB GPU). A server keeps the states
+ * of many sequences in one cache of n_slots rows, conv_cache (n_slots, d_inner, d_conv-1)
+ * act dtype and ssm_cache (n_slots, d_inner, d_state) fp32, and runs each call on whichever
+ * sequences are active: continuous batching, prefill in chunks that continue from the
+ * carried state, and mixed batches (a decode token is a one-token sequence that continues
+ * from its slot). States are read from and written to their slots in place.
+ */
+
+/* Workspace for jamba_mamba_prefill_slots (the prefill's, plus n_seqs final states). */
+jm_status jm_prefill_slots_workspace_size(const jm_layer_dims *dims, int32_t n_seqs,
+                                          int64_t total_tokens, size_t *bytes);
+
+/*
+ * Prefill over packed sequences against the state cache. Sequence i starts from slot
+ * init_slots[i] (-1: from zeros) and leaves its final states in slot final_slots[i] (-1:
+ * not kept). init_slots / final_slots are device arrays of n_seqs int32 with host copies
+ * (*_host, equal values) used for validation; either pair may be NULL (all -1). A final
+ * slot may be its own sequence's init slot (continue in place) but no other sequence's init
+ * slot, and final slots are distinct. Other arguments as in jamba_mamba_prefill; workspace
+ * >= jm_prefill_slots_workspace_size bytes.
+ */
+jm_status jamba_mamba_prefill_slots(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                                    const void *u, const int32_t *cu_seqlens,
+                                    const int32_t *cu_seqlens_host, int32_t n_seqs,
+                                    int64_t total_tokens, const int32_t *init_slots,
+                                    const int32_t *init_slots_host, const int32_t *final_slots,
+                                    const int32_t *final_slots_host, void *conv_cache,
+                                    float *ssm_cache, int32_t n_slots, void *out, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for `batch` sequences whose states sit in slots slots[0..batch) of the
+ * cache (device int32 array, distinct values in [0, n_slots), with an equal host copy
+ * slots_host for validation); the slots are updated in place. u, out, workspace as in
+ * jamba_mamba_decode_step (workspace >= jm_decode_workspace_size(batch)).
+ */
+jm_status jamba_mamba_decode_step_slots(const jm_layer_dims *dims,
+                                        const jm_layer_weights *weights, const void *u,
+                                        int32_t batch, const int32_t *slots,
+                                        const int32_t *slots_host, void *conv_cache,
+                                        float *ssm_cache, int32_t n_slots, void *out,
+                                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- Plan inspection (host only; for tests of the packed-sequence indexing) ---- */
 
 /* One run of consecutive tokens inside one scan chunk that belong to one sequence. */

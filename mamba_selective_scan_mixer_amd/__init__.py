@@ -106,11 +106,20 @@ def lib() -> ctypes.CDLL:
         L.jm_stage_scan.argtypes = [D, W, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                     ctypes.c_int64, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.jm_stage_out_proj.argtypes = [D, W, _P, ctypes.c_int64, _P, _P]
+        L.jm_prefill_slots_workspace_size.argtypes = [D, ctypes.c_int32, ctypes.c_int64,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+        L.jamba_mamba_prefill_slots.argtypes = [
+            D, W, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
+            ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+        L.jamba_mamba_decode_step_slots.argtypes = [
+            D, W, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
         for name in ("jm_prefill_workspace_size", "jm_decode_workspace_size", "jamba_mamba_prefill",
                      "jamba_mamba_decode_step", "jm_prefill_plan", "jm_set_scan_chunk_len",
                      "jm_profile_enable", "jm_profile_reset", "jm_profile_read",
                      "jm_stage_in_proj", "jm_stage_conv", "jm_stage_x_proj", "jm_stage_dt_proj",
-                     "jm_stage_scan_workspace_size", "jm_stage_scan", "jm_stage_out_proj"):
+                     "jm_stage_scan_workspace_size", "jm_stage_scan", "jm_stage_out_proj",
+                     "jm_prefill_slots_workspace_size", "jamba_mamba_prefill_slots",
+                     "jamba_mamba_decode_step_slots"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -415,4 +424,96 @@ def jm_stage_out_proj(layer: MambaLayer, g: torch.Tensor, stream=None):
     out = torch.empty((T, d.d_model), dtype=dt, device=g.device)
     _check(lib().jm_stage_out_proj(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(g), T,
                                    _ptr(out), _stream(stream)))
+    return out
+
+
+# ---- state cache (serving) ------------------------------------------------------------------
+
+class StateCache:
+    """Conv and SSM states of n_slots sequences: conv (n_slots, d_inner, d_conv-1) in the
+    activation dtype and ssm (n_slots, d_inner, d_state) fp32, zero-initialised."""
+
+    def __init__(self, dims: LayerDims, n_slots: int, device="cuda"):
+        self.dims = dims
+        self.n_slots = n_slots
+        self.conv = torch.zeros((n_slots, dims.d_inner, dims.d_conv - 1), dtype=_torch_dtype(dims),
+                                device=device)
+        self.ssm = torch.zeros((n_slots, dims.d_inner, dims.d_state), dtype=torch.float32,
+                               device=device)
+
+
+def _slot_arrays(slots, n: int, device):
+    """(device int32 tensor, host ctypes array) for a list of n slot ids, or (None, None)."""
+    if slots is None:
+        return None, None
+    vals = [int(v) for v in slots]
+    if len(vals) != n:
+        raise ValueError(f"need {n} slot ids, got {len(vals)}")
+    return (torch.tensor(vals, dtype=torch.int32, device=device),
+            (ctypes.c_int32 * n)(*vals))
+
+
+def prefill_slots_workspace_size(dims: LayerDims, n_seqs: int, total_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jm_prefill_slots_workspace_size(ctypes.byref(dims), n_seqs, total_tokens,
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def jamba_mamba_prefill_slots(layer: MambaLayer, u: torch.Tensor, cu_seqlens: torch.Tensor,
+                              cu_seqlens_host: Sequence[int], cache: StateCache,
+                              init_slots=None, final_slots=None, out=None, workspace=None,
+                              stream=None):
+    """Prefill against a state cache: sequence i starts from slot init_slots[i] (-1: zeros)
+    and leaves its states in slot final_slots[i] (-1: not kept). Returns out."""
+    d = layer.dims
+    dt = _torch_dtype(d)
+    host, n = _host_cu(cu_seqlens_host)
+    T = host[n] if n > 0 else 0
+    _need(u, "u", dt, (T, d.d_model))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,))
+    _need(cache.conv, "cache.conv", dt, (cache.n_slots, d.d_inner, d.d_conv - 1))
+    _need(cache.ssm, "cache.ssm", torch.float32, (cache.n_slots, d.d_inner, d.d_state))
+    if out is None:
+        out = torch.empty((T, d.d_model), dtype=dt, device=u.device)
+    _need(out, "out", dt, (T, d.d_model))
+    i_dev, i_host = _slot_arrays(init_slots, n, u.device)
+    f_dev, f_host = _slot_arrays(final_slots, n, u.device)
+    need = prefill_slots_workspace_size(d, n, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    _check(lib().jamba_mamba_prefill_slots(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), _ptr(cu_seqlens), host, n, T,
+        _ptr(i_dev), i_host, _ptr(f_dev), f_host, _ptr(cache.conv), _ptr(cache.ssm),
+        cache.n_slots, _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def jamba_mamba_decode_step_slots(layer: MambaLayer, u: torch.Tensor, cache: StateCache,
+                                  slots: Sequence[int], out=None, workspace=None, stream=None,
+                                  slots_device: Optional[torch.Tensor] = None):
+    """One token for each of len(slots) sequences whose states are in those cache slots
+    (updated in place). Returns out. slots_device: an int32 device copy of `slots` to reuse
+    (e.g. inside a captured graph); made here when not given."""
+    d = layer.dims
+    dt = _torch_dtype(d)
+    b = len(slots)
+    _need(u, "u", dt, (b, d.d_model))
+    _need(cache.conv, "cache.conv", dt, (cache.n_slots, d.d_inner, d.d_conv - 1))
+    _need(cache.ssm, "cache.ssm", torch.float32, (cache.n_slots, d.d_inner, d.d_state))
+    if out is None:
+        out = torch.empty((b, d.d_model), dtype=dt, device=u.device)
+    _need(out, "out", dt, (b, d.d_model))
+    vals = [int(v) for v in slots]
+    host = (ctypes.c_int32 * b)(*vals)
+    if slots_device is None:
+        slots_device = torch.tensor(vals, dtype=torch.int32, device=u.device)
+    _need(slots_device, "slots_device", torch.int32, (b,))
+    need = decode_workspace_size(d, b)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=u.device)
+    _check(lib().jamba_mamba_decode_step_slots(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), b, _ptr(slots_device), host,
+        _ptr(cache.conv), _ptr(cache.ssm), cache.n_slots, _ptr(out), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
     return out

@@ -241,17 +241,19 @@ jm_status step_in_proj(const jm_layer_dims& d, const jm_layer_weights& w, const 
   return JM_OK;
 }
 
+// init_rows / final_rows: state row (slot) of each sequence, -1 = none; NULL = row i.
 template <typename T>
 jm_status step_conv(const jm_layer_dims& d, const jm_layer_weights& w, const T* x,
                     const int32_t* cu, int32_t n_seqs, int64_t n_tok, const T* init_conv,
-                    T* xh, T* final_conv, hipStream_t stream) {
+                    T* xh, T* final_conv, hipStream_t stream,
+                    const int32_t* init_rows = nullptr, const int32_t* final_rows = nullptr) {
   JM_LAUNCH("conv1d_silu",
             launch_conv_silu<T>(x, xh, static_cast<const T*>(w.conv_w),
-                                static_cast<const T*>(w.conv_b), init_conv, cu, n_seqs, n_tok,
-                                d.d_inner, stream));
+                                static_cast<const T*>(w.conv_b), init_conv, init_rows, cu, n_seqs,
+                                n_tok, d.d_inner, stream));
   if (final_conv)
-    JM_LAUNCH("conv_final",
-              launch_conv_final<T>(x, init_conv, final_conv, cu, n_seqs, d.d_inner, stream));
+    JM_LAUNCH("conv_final", launch_conv_final<T>(x, init_conv, init_rows, final_conv, final_rows,
+                                                 cu, n_seqs, d.d_inner, stream));
   return JM_OK;
 }
 
@@ -290,7 +292,7 @@ jm_status step_scan(const jm_layer_dims& d, const jm_layer_weights& w, const T* 
                     const float* dt, const float* Bm, const float* Cm, const T* z,
                     const int32_t* cu, int32_t n_seqs, int64_t n_tok, const float* init_ssm,
                     T* g, float* final_ssm, char* agg, int32_t chunk_len, int32_t n_chunks,
-                    hipStream_t stream) {
+                    hipStream_t stream, const int32_t* init_rows = nullptr) {
   const size_t ab = scan_agg_bytes(d, n_chunks);
   float* aggP = reinterpret_cast<float*>(agg);
   float* aggh = reinterpret_cast<float*>(agg + ab);
@@ -298,14 +300,14 @@ jm_status step_scan(const jm_layer_dims& d, const jm_layer_weights& w, const T* 
   const int di = d.d_inner;
   if (n_chunks > 1) {
     JM_LAUNCH("scan_chunk_state",
-              launch_scan_chunk_state<T>(xh, dt, w.A_log, Bm, init_ssm, cu, aggP, aggh, n_seqs,
-                                         n_tok, di, chunk_len, n_chunks - 1, stream));
+              launch_scan_chunk_state<T>(xh, dt, w.A_log, Bm, init_ssm, init_rows, cu, aggP, aggh,
+                                         n_seqs, n_tok, di, chunk_len, n_chunks - 1, stream));
     JM_LAUNCH("scan_chunk_carry", launch_scan_chunk_carry(aggP, aggh, carry, di, n_chunks, stream));
   }
   JM_LAUNCH("scan_chunk_output",
-            launch_scan_chunk_output<T>(xh, dt, w.A_log, Bm, Cm, w.D, z, g, init_ssm, final_ssm,
-                                        n_chunks > 1 ? carry : nullptr, cu, n_seqs, n_tok, di,
-                                        chunk_len, n_chunks, stream));
+            launch_scan_chunk_output<T>(xh, dt, w.A_log, Bm, Cm, w.D, z, g, init_ssm, init_rows,
+                                        final_ssm, n_chunks > 1 ? carry : nullptr, cu, n_seqs,
+                                        n_tok, di, chunk_len, n_chunks, stream));
   return JM_OK;
 }
 
@@ -319,11 +321,17 @@ jm_status step_out_proj(const jm_layer_dims& d, const jm_layer_weights& w, const
   return JM_OK;
 }
 
+// With slot maps (init_rows / final_rows, device arrays): the states live in caches of
+// n_slots rows; init_conv / init_ssm and final_conv are the caches, and final_ssm_tmp is a
+// per-sequence workspace buffer that is scattered into the SSM cache (final_ssm_cache)
+// after the scan, so no sequence's state is overwritten while another chunk still reads it.
 template <typename T>
 jm_status run_prefill(const jm_layer_dims& d, const jm_layer_weights& w, const T* u,
                       const int32_t* cu, int32_t n_seqs, int64_t n_tok, const T* init_conv,
                       const float* init_ssm, T* out, T* final_conv, float* final_ssm,
-                      char* ws, int32_t chunk_len, int32_t n_chunks, hipStream_t stream) {
+                      char* ws, int32_t chunk_len, int32_t n_chunks, hipStream_t stream,
+                      const int32_t* init_rows = nullptr, const int32_t* final_rows = nullptr,
+                      float* final_ssm_cache = nullptr) {
   const PrefillLayout L = prefill_layout(d, n_tok, n_chunks);
   T* x = reinterpret_cast<T*>(ws + L.x);
   T* z = reinterpret_cast<T*>(ws + L.z);
@@ -335,20 +343,27 @@ jm_status run_prefill(const jm_layer_dims& d, const jm_layer_weights& w, const T
   T* g = x;  // x is dead once the conv and its final state are done
   jm_status st;
   if ((st = step_in_proj<T>(d, w, u, n_tok, x, z, stream)) != JM_OK) return st;
-  if ((st = step_conv<T>(d, w, x, cu, n_seqs, n_tok, init_conv, xh, final_conv, stream)) != JM_OK)
+  if ((st = step_conv<T>(d, w, x, cu, n_seqs, n_tok, init_conv, xh, final_conv, stream,
+                         init_rows, final_rows)) != JM_OK)
     return st;
   if ((st = step_x_proj<T>(d, w, xh, n_tok, delta, Bm, Cm, stream)) != JM_OK) return st;
   if ((st = step_dt_proj<T>(d, w, delta, n_tok, dt, stream)) != JM_OK) return st;
   if ((st = step_scan<T>(d, w, xh, dt, Bm, Cm, z, cu, n_seqs, n_tok, init_ssm, g, final_ssm,
-                         ws + L.agg, chunk_len, n_chunks, stream)) != JM_OK)
+                         ws + L.agg, chunk_len, n_chunks, stream, init_rows)) != JM_OK)
     return st;
+  if (final_ssm_cache && final_rows)
+    JM_LAUNCH("state_scatter", launch_scatter_rows(final_ssm, final_ssm_cache, final_rows, n_seqs,
+                                                   (int64_t)d.d_inner * 16, stream));
   if ((st = step_out_proj<T>(d, w, g, n_tok, out, stream)) != JM_OK) return st;
   return ok();
 }
 
+// rows (device, batch entries) maps batch row -> state row (slot) of conv_state / ssm_state;
+// NULL: batch row b uses state row b.
 template <typename T>
 jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T* u, int32_t b,
-                     T* conv_state, float* ssm_state, T* out, char* ws, hipStream_t stream) {
+                     T* conv_state, float* ssm_state, T* out, char* ws, hipStream_t stream,
+                     const int32_t* rows = nullptr) {
   const DecodeLayout L = decode_layout(d, b);
   T* x = reinterpret_cast<T*>(ws + L.x);
   T* z = reinterpret_cast<T*>(ws + L.z);
@@ -366,12 +381,15 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
       for (int32_t b0 = 0; b0 < b; b0 += 64) {
         const int M = b - b0 < 64 ? b - b0 : 64;
         const bf16* ut = u + (int64_t)b0 * dm;
-        bf16* ct = conv_state + (int64_t)b0 * di * 3;
-        float* st = ssm_state + (int64_t)b0 * di * 16;
+        // without a slot map, the tile's states are the next M rows; with one, the tile's
+        // entries of the map index the whole caches
+        bf16* ct = rows ? conv_state : conv_state + (int64_t)b0 * di * 3;
+        float* st = rows ? ssm_state : ssm_state + (int64_t)b0 * di * 16;
+        const int32_t* rt = rows ? rows + b0 : nullptr;
         bf16* ot = out + (int64_t)b0 * dm;
         JM_LAUNCH("dec_in_proj", launch_dec_in_proj(ut, Win, static_cast<const bf16*>(w.conv_w),
-                                                    static_cast<const bf16*>(w.conv_b), ct, xh, z,
-                                                    M, dm, di, stream));
+                                                    static_cast<const bf16*>(w.conv_b), ct, rt, xh,
+                                                    z, M, dm, di, stream));
         JM_LAUNCH("dec_x_proj", launch_dec_x_proj(xh, static_cast<const bf16*>(w.x_proj_w),
                                                   partial, delta, Bm, Cm, M, di, R, stream));
         if (w.dt_norm_w)
@@ -380,8 +398,8 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
                                                w.norm_eps, M, R, stream));
         JM_LAUNCH("dec_update", launch_dec_update(xh, z, delta, Bm, Cm,
                                                   static_cast<const bf16*>(w.dt_proj_w),
-                                                  w.dt_proj_b, w.A_log, w.D, st, g, M, di, R,
-                                                  stream));
+                                                  w.dt_proj_b, w.A_log, w.D, st, rt, g, M, di,
+                                                  R, stream));
         JM_LAUNCH("dec_out_proj", launch_dec_out_proj(g, static_cast<const bf16*>(w.out_proj_w),
                                                       partial, ot, M, dm, di, stream));
       }
@@ -393,7 +411,8 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
   e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = di;
   JM_LAUNCH("dec_in_proj", gemm<T>(u, dm, static_cast<const T*>(w.in_proj_w), dm, b, 2 * di, dm,
                                    e, stream));
-  JM_LAUNCH("dec_conv", launch_decode_conv<T>(x, xh, conv_state, static_cast<const T*>(w.conv_w),
+  JM_LAUNCH("dec_conv", launch_decode_conv<T>(x, xh, conv_state, rows,
+                                              static_cast<const T*>(w.conv_w),
                                               static_cast<const T*>(w.conv_b), b, di, stream));
   e = epi_none();
   e.kind = EPI_XPROJ; e.out0 = delta; e.outf0 = Bm; e.outf1 = Cm; e.split = R; e.n_state = 16;
@@ -404,7 +423,8 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
                                                         w.C_norm_w, w.norm_eps, b, R, stream));
   JM_LAUNCH("dec_update",
             launch_decode_update<T>(xh, z, delta, Bm, Cm, static_cast<const T*>(w.dt_proj_w),
-                                    w.dt_proj_b, w.A_log, w.D, ssm_state, g, b, di, R, stream));
+                                    w.dt_proj_b, w.A_log, w.D, ssm_state, rows, g, b, di, R,
+                                    stream));
   e = epi_none();
   e.kind = EPI_STORE; e.out0 = out; e.ldo = dm;
   JM_LAUNCH("dec_out_proj", gemm<T>(g, di, static_cast<const T*>(w.out_proj_w), di, b, dm, di, e,
@@ -436,6 +456,58 @@ jm_status check_ptrs(std::initializer_list<const void*> required,
 }
 
 bool is_bf16(const jm_layer_dims* d) { return d->act_dtype == JM_BF16; }
+
+
+// ---- state-cache (slot) entry points: validation of the slot arrays ------------------------
+// Prefill: init slots in [-1, n_slots); final slots in [-1, n_slots), distinct where >= 0, and
+// never another sequence's init slot (a sequence may write back to its own init slot).
+jm_status check_prefill_slots(const int32_t* init_dev, const int32_t* init_host,
+                              const int32_t* final_dev, const int32_t* final_host, int32_t n_seqs,
+                              int32_t n_slots) {
+  if ((init_dev == nullptr) != (init_host == nullptr) ||
+      (final_dev == nullptr) != (final_host == nullptr))
+    return fail(JM_ERR_INVALID_ARG, "slot arrays need both the device and the host copy (or neither)");
+  std::vector<int32_t> owner((size_t)n_slots, -1);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t a = init_host ? init_host[i] : -1;
+    const int32_t b = final_host ? final_host[i] : -1;
+    if (a < -1 || a >= n_slots || b < -1 || b >= n_slots)
+      return fail(JM_ERR_SHAPE, "sequence %d: slot out of range (init %d, final %d, n_slots %d)",
+                  i, a, b, n_slots);
+    if (b >= 0) {
+      if (owner[b] >= 0)
+        return fail(JM_ERR_INVALID_ARG, "final slot %d is written by sequences %d and %d", b,
+                    owner[b], i);
+      owner[b] = i;
+    }
+  }
+  if (init_host && final_host)
+    for (int32_t j = 0; j < n_seqs; ++j) {
+      const int32_t a = init_host[j];
+      if (a >= 0 && owner[a] >= 0 && owner[a] != j)
+        return fail(JM_ERR_INVALID_ARG, "slot %d is sequence %d's initial state and sequence "
+                    "%d's final state", a, j, owner[a]);
+    }
+  return JM_OK;
+}
+
+jm_status check_decode_slots(const int32_t* dev, const int32_t* host, int32_t batch,
+                             int32_t n_slots) {
+  if (!dev || !host) return fail(JM_ERR_INVALID_ARG, "slots and slots_host must not be NULL");
+  std::vector<char> used((size_t)n_slots, 0);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t v = host[b];
+    if (v < 0 || v >= n_slots)
+      return fail(JM_ERR_SHAPE, "batch row %d: slot %d out of range [0, %d)", b, v, n_slots);
+    if (used[v]) return fail(JM_ERR_INVALID_ARG, "slot %d appears twice in the batch", v);
+    used[v] = 1;
+  }
+  return JM_OK;
+}
+
+size_t slots_tmp_bytes(const jm_layer_dims& d, int32_t n_seqs) {
+  return align256((size_t)n_seqs * d.d_inner * 16 * sizeof(float));
+}
 
 }  // namespace
 
@@ -608,6 +680,93 @@ jm_status jamba_mamba_decode_step(const jm_layer_dims* dims, const jm_layer_weig
   return run_decode<float>(*dims, *weights, static_cast<const float*>(u), batch,
                            static_cast<float*>(conv_state), ssm_state, static_cast<float*>(out), ws,
                            s);
+}
+
+// ---- state-cache (slot) entry points -----------------------------------------------------
+jm_status jm_prefill_slots_workspace_size(const jm_layer_dims* dims, int32_t n_seqs,
+                                          int64_t total_tokens, size_t* bytes) {
+  jm_status st = jm_prefill_workspace_size(dims, n_seqs, total_tokens, bytes);
+  if (st != JM_OK) return st;
+  if (total_tokens > 0) *bytes += slots_tmp_bytes(*dims, n_seqs);
+  return ok();
+}
+
+jm_status jamba_mamba_prefill_slots(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                                    const void* u, const int32_t* cu_seqlens,
+                                    const int32_t* cu_seqlens_host, int32_t n_seqs,
+                                    int64_t total_tokens, const int32_t* init_slots,
+                                    const int32_t* init_slots_host, const int32_t* final_slots,
+                                    const int32_t* final_slots_host, void* conv_cache,
+                                    float* ssm_cache, int32_t n_slots, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream_ptr) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK || (st = check_weights(weights)) != JM_OK) return st;
+  if (n_seqs < 0 || total_tokens < 0 || n_slots < 1)
+    return fail(JM_ERR_INVALID_ARG, "negative size or n_slots < 1");
+  if (total_tokens >= ((int64_t)1 << 31)) return fail(JM_ERR_SHAPE, "total_tokens must be < 2^31");
+  if (n_seqs == 0 || total_tokens == 0) {
+    if (n_seqs != 0 || total_tokens != 0)
+      return fail(JM_ERR_SHAPE, "n_seqs = %d with total_tokens = %lld", n_seqs,
+                  (long long)total_tokens);
+    return ok();
+  }
+  if (!cu_seqlens) return fail(JM_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if ((st = check_cu(cu_seqlens_host, n_seqs, total_tokens)) != JM_OK) return st;
+  if ((st = check_ptrs({u, out, conv_cache, ssm_cache}, {workspace})) != JM_OK) return st;
+  if ((st = check_prefill_slots(init_slots, init_slots_host, final_slots, final_slots_host,
+                                n_seqs, n_slots)) != JM_OK)
+    return st;
+  int32_t cl, nc;
+  plan_chunks(*dims, total_tokens, &cl, &nc);
+  const size_t base = prefill_layout(*dims, total_tokens, nc).total;
+  const size_t need = base + slots_tmp_bytes(*dims, n_seqs);
+  if (!workspace || workspace_bytes < need)
+    return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  char* ws = static_cast<char*>(workspace);
+  float* tmp = final_slots ? reinterpret_cast<float*>(ws + base) : nullptr;
+  const float* init_ssm = init_slots ? ssm_cache : nullptr;
+  if (dims->act_dtype == JM_BF16) {
+    bf16* cc = static_cast<bf16*>(conv_cache);
+    return run_prefill<bf16>(*dims, *weights, static_cast<const bf16*>(u), cu_seqlens, n_seqs,
+                             total_tokens, init_slots ? cc : nullptr, init_ssm,
+                             static_cast<bf16*>(out), final_slots ? cc : nullptr, tmp, ws, cl, nc,
+                             s, init_slots, final_slots, ssm_cache);
+  }
+  float* cc = static_cast<float*>(conv_cache);
+  return run_prefill<float>(*dims, *weights, static_cast<const float*>(u), cu_seqlens, n_seqs,
+                            total_tokens, init_slots ? cc : nullptr, init_ssm,
+                            static_cast<float*>(out), final_slots ? cc : nullptr, tmp, ws, cl, nc,
+                            s, init_slots, final_slots, ssm_cache);
+}
+
+jm_status jamba_mamba_decode_step_slots(const jm_layer_dims* dims,
+                                        const jm_layer_weights* weights, const void* u,
+                                        int32_t batch, const int32_t* slots,
+                                        const int32_t* slots_host, void* conv_cache,
+                                        float* ssm_cache, int32_t n_slots, void* out,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream_ptr) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK || (st = check_weights(weights)) != JM_OK) return st;
+  if (batch < 0 || n_slots < 1) return fail(JM_ERR_INVALID_ARG, "negative batch or n_slots < 1");
+  if (batch == 0) return ok();
+  if ((st = check_ptrs({u, conv_cache, ssm_cache, out}, {workspace})) != JM_OK) return st;
+  if ((st = check_decode_slots(slots, slots_host, batch, n_slots)) != JM_OK) return st;
+  const size_t need = decode_layout(*dims, batch).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
+  char* ws = static_cast<char*>(workspace);
+  if (dims->act_dtype == JM_BF16)
+    return run_decode<bf16>(*dims, *weights, static_cast<const bf16*>(u), batch,
+                            static_cast<bf16*>(conv_cache), ssm_cache, static_cast<bf16*>(out),
+                            ws, s, slots);
+  return run_decode<float>(*dims, *weights, static_cast<const float*>(u), batch,
+                           static_cast<float*>(conv_cache), ssm_cache, static_cast<float*>(out),
+                           ws, s, slots);
 }
 
 // ---- stage entry points ------------------------------------------------------------------

@@ -52,20 +52,28 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n_se
   return lo;
 }
 
+// State row of sequence (or batch row) i: rows[i] when a slot map is given (-1 = no
+// state: zeros / nothing written), else i.
+__device__ __forceinline__ int64_t state_row(const int32_t* rows, int i) {
+  return rows ? (int64_t)rows[i] : (int64_t)i;
+}
+
 // History value of channel d, `back` (1..3) positions before sequence i's start.
 template <typename T>
-__device__ __forceinline__ float hist(const T* __restrict__ init, int i, int d_inner, int d,
-                                      int back) {
-  if (init == nullptr) return 0.0f;
-  return to_f32(init[((int64_t)i * d_inner + d) * (KC - 1) + (KC - 1 - back)]);
+__device__ __forceinline__ float hist(const T* __restrict__ init, const int32_t* rows, int i,
+                                      int d_inner, int d, int back) {
+  const int64_t r = state_row(rows, i);
+  if (init == nullptr || r < 0) return 0.0f;
+  return to_f32(init[(r * d_inner + d) * (KC - 1) + (KC - 1 - back)]);
 }
 
 template <typename T>
 __global__ __launch_bounds__(256)
 void conv_silu_kernel(const T* __restrict__ x, T* __restrict__ xh,
                       const T* __restrict__ conv_w, const T* __restrict__ conv_b,
-                      const T* __restrict__ init, const int32_t* __restrict__ cu,
-                      int n_seqs, int64_t n_tok, int d_inner, int run_len) {
+                      const T* __restrict__ init, const int32_t* __restrict__ init_rows,
+                      const int32_t* __restrict__ cu, int n_seqs, int64_t n_tok, int d_inner,
+                      int run_len) {
   const int d0 = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
   if (d0 >= d_inner) return;
   const int64_t t0 = (int64_t)blockIdx.y * run_len;
@@ -92,7 +100,7 @@ void conv_silu_kernel(const T* __restrict__ x, T* __restrict__ xh,
     } else {
       int back = (int)(s_begin - p);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) win[q][j] = hist(init, i, d_inner, d0 + j, back);
+      for (int j = 0; j < VEC; ++j) win[q][j] = hist(init, init_rows, i, d_inner, d0 + j, back);
     }
   }
   for (int64_t t = t0; t < t1; ++t) {
@@ -103,7 +111,8 @@ void conv_silu_kernel(const T* __restrict__ x, T* __restrict__ xh,
 #pragma unroll
       for (int q = 0; q < KC - 1; ++q)
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) win[q][j] = hist(init, i, d_inner, d0 + j, KC - 1 - q);
+        for (int j = 0; j < VEC; ++j)
+          win[q][j] = hist(init, init_rows, i, d_inner, d0 + j, KC - 1 - q);
     }
     float cur[VEC], out[VEC];
     load8(x + t * d_inner + d0, cur);
@@ -125,14 +134,19 @@ void conv_silu_kernel(const T* __restrict__ x, T* __restrict__ xh,
 
 // Final conv state of each sequence: its last three pre-conv values, oldest first
 // (reaching into the initial state for sequences shorter than three tokens). All
-// three values are read before any is written, so final may alias init.
+// three values are read before any is written, so final may alias init (the same row,
+// or with slot maps the same slot).
 template <typename T>
 __global__ __launch_bounds__(256)
-void conv_final_kernel(const T* __restrict__ x, const T* init, T* final_state,
+void conv_final_kernel(const T* __restrict__ x, const T* init, const int32_t* init_rows,
+                       T* final_state, const int32_t* final_rows,
                        const int32_t* __restrict__ cu, int d_inner) {
   const int d = blockIdx.x * blockDim.x + threadIdx.x;
   const int i = blockIdx.y;
   if (d >= d_inner) return;
+  const int64_t rf = state_row(final_rows, i);
+  if (rf < 0) return;
+  const int64_t ri = state_row(init_rows, i);
   const int64_t s = cu[i], e = cu[i + 1];
   T v[KC - 1];
 #pragma unroll
@@ -142,24 +156,24 @@ void conv_final_kernel(const T* __restrict__ x, const T* init, T* final_state,
       v[q] = x[p * d_inner + d];
     } else {
       int back = (int)(s - p);
-      v[q] = init ? init[((int64_t)i * d_inner + d) * (KC - 1) + (KC - 1 - back)]
-                  : from_f32<T>(0.0f);
+      v[q] = (init && ri >= 0) ? init[(ri * d_inner + d) * (KC - 1) + (KC - 1 - back)]
+                               : from_f32<T>(0.0f);
     }
   }
 #pragma unroll
-  for (int q = 0; q < KC - 1; ++q) final_state[((int64_t)i * d_inner + d) * (KC - 1) + q] = v[q];
+  for (int q = 0; q < KC - 1; ++q) final_state[(rf * d_inner + d) * (KC - 1) + q] = v[q];
 }
 
 // Decode: one token per sequence; shift the window in place.
 template <typename T>
 __global__ __launch_bounds__(256)
 void decode_conv_kernel(const T* __restrict__ x, T* __restrict__ xh, T* __restrict__ state,
-                        const T* __restrict__ conv_w, const T* __restrict__ conv_b,
-                        int d_inner) {
+                        const int32_t* __restrict__ rows, const T* __restrict__ conv_w,
+                        const T* __restrict__ conv_b, int d_inner) {
   const int d = blockIdx.x * blockDim.x + threadIdx.x;
   const int bidx = blockIdx.y;
   if (d >= d_inner) return;
-  T* st = state + ((int64_t)bidx * d_inner + d) * (KC - 1);
+  T* st = state + (state_row(rows, bidx) * d_inner + d) * (KC - 1);
   float s0 = to_f32(st[0]), s1 = to_f32(st[1]), s2 = to_f32(st[2]);
   T xr = x[(int64_t)bidx * d_inner + d];
   float xv = to_f32(xr);
@@ -179,8 +193,8 @@ void decode_conv_kernel(const T* __restrict__ x, T* __restrict__ xh, T* __restri
 
 template <typename T>
 hipError_t launch_conv_silu(const T* x, T* xh, const T* conv_w, const T* conv_b,
-                            const T* init_conv, const int32_t* cu, int n_seqs, int64_t n_tok,
-                            int d_inner, hipStream_t s) {
+                            const T* init_conv, const int32_t* init_rows, const int32_t* cu,
+                            int n_seqs, int64_t n_tok, int d_inner, hipStream_t s) {
   if (n_tok <= 0) return hipSuccess;
   const int groups = d_inner / VEC;
   const int block = groups >= 256 ? 256 : ((groups + 63) / 64) * 64;
@@ -188,43 +202,42 @@ hipError_t launch_conv_silu(const T* x, T* xh, const T* conv_w, const T* conv_b,
   while ((n_tok + run - 1) / run > 65535) run *= 2;
   dim3 grid((groups + block - 1) / block, (unsigned)((n_tok + run - 1) / run));
   hipLaunchKernelGGL(conv_silu_kernel<T>, grid, dim3(block), 0, s, x, xh, conv_w, conv_b,
-                     init_conv, cu, n_seqs, n_tok, d_inner, (int)run);
+                     init_conv, init_rows, cu, n_seqs, n_tok, d_inner, (int)run);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_conv_final(const T* x, const T* init_conv, T* final_conv, const int32_t* cu,
+hipError_t launch_conv_final(const T* x, const T* init_conv, const int32_t* init_rows,
+                             T* final_conv, const int32_t* final_rows, const int32_t* cu,
                              int n_seqs, int d_inner, hipStream_t s) {
   if (n_seqs <= 0) return hipSuccess;
   dim3 grid((d_inner + 255) / 256, n_seqs);
-  hipLaunchKernelGGL(conv_final_kernel<T>, grid, dim3(256), 0, s, x, init_conv, final_conv, cu,
-                     d_inner);
+  hipLaunchKernelGGL(conv_final_kernel<T>, grid, dim3(256), 0, s, x, init_conv, init_rows,
+                     final_conv, final_rows, cu, d_inner);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_decode_conv(const T* x, T* xh, T* conv_state, const T* conv_w,
-                              const T* conv_b, int batch, int d_inner, hipStream_t s) {
+hipError_t launch_decode_conv(const T* x, T* xh, T* conv_state, const int32_t* rows,
+                              const T* conv_w, const T* conv_b, int batch, int d_inner,
+                              hipStream_t s) {
   if (batch <= 0) return hipSuccess;
   dim3 grid((d_inner + 255) / 256, batch);
-  hipLaunchKernelGGL(decode_conv_kernel<T>, grid, dim3(256), 0, s, x, xh, conv_state, conv_w,
-                     conv_b, d_inner);
+  hipLaunchKernelGGL(decode_conv_kernel<T>, grid, dim3(256), 0, s, x, xh, conv_state, rows,
+                     conv_w, conv_b, d_inner);
   return hipGetLastError();
 }
 
-template hipError_t launch_conv_silu<float>(const float*, float*, const float*, const float*,
-                                            const float*, const int32_t*, int, int64_t, int,
-                                            hipStream_t);
-template hipError_t launch_conv_silu<bf16>(const bf16*, bf16*, const bf16*, const bf16*,
-                                           const bf16*, const int32_t*, int, int64_t, int,
-                                           hipStream_t);
-template hipError_t launch_conv_final<float>(const float*, const float*, float*, const int32_t*,
-                                             int, int, hipStream_t);
-template hipError_t launch_conv_final<bf16>(const bf16*, const bf16*, bf16*, const int32_t*, int,
-                                            int, hipStream_t);
-template hipError_t launch_decode_conv<float>(const float*, float*, float*, const float*,
-                                              const float*, int, int, hipStream_t);
-template hipError_t launch_decode_conv<bf16>(const bf16*, bf16*, bf16*, const bf16*,
-                                             const bf16*, int, int, hipStream_t);
+#define JM_CONV_INST(T)                                                                        \
+  template hipError_t launch_conv_silu<T>(const T*, T*, const T*, const T*, const T*,           \
+                                          const int32_t*, const int32_t*, int, int64_t, int,     \
+                                          hipStream_t);                                          \
+  template hipError_t launch_conv_final<T>(const T*, const T*, const int32_t*, T*,               \
+                                           const int32_t*, const int32_t*, int, int,             \
+                                           hipStream_t);                                         \
+  template hipError_t launch_decode_conv<T>(const T*, T*, T*, const int32_t*, const T*, const T*,\
+                                            int, int, hipStream_t);
+JM_CONV_INST(float)
+JM_CONV_INST(bf16)
 
 }  // namespace jm

@@ -31,7 +31,8 @@ struct DecEpiArgs {
   bf16* out;             // STORE: (M, N) bf16
   bf16* xh;              // INPROJ: (M, d_inner) conv+SiLU output
   bf16* z;               // INPROJ: (M, d_inner)
-  bf16* conv_state;      // INPROJ: (M, d_inner, 3) in/out
+  bf16* conv_state;      // INPROJ: (rows, d_inner, 3) in/out
+  const int32_t* rows;   // INPROJ: state row of token row m (NULL: m)
   const bf16* conv_w;    // INPROJ: (d_inner, 4)
   const bf16* conv_b;    // INPROJ: (d_inner) or null
   int d_inner;           // INPROJ split point
@@ -168,7 +169,7 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
     } else {
       const int di = e.d_inner;
       if (n < di) {
-        bf16* st = e.conv_state + ((int64_t)m * di + n) * 3;
+        bf16* st = e.conv_state + ((e.rows ? (int64_t)e.rows[m] : (int64_t)m) * di + n) * 3;
         const bf16 xb = from_f32<bf16>(v);
         const float s0 = to_f32(st[0]), s1 = to_f32(st[1]), s2 = to_f32(st[2]);
         const bf16* cw = e.conv_w + (int64_t)n * 4;
@@ -228,7 +229,8 @@ void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
                        const float* __restrict__ Cm, const bf16* __restrict__ W_dt,
                        const float* __restrict__ b_dt, const float* __restrict__ A_log,
                        const float* __restrict__ Dv, float* __restrict__ state,
-                       bf16* __restrict__ g, int M, int d_inner, int R) {
+                       const int32_t* __restrict__ rows, bf16* __restrict__ g, int M,
+                       int d_inner, int R) {
   __shared__ float sdt[4][UPD_MT][UPD_CH + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -269,7 +271,8 @@ void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
     const float xv = to_f32(xh[o]);
     const float zv = to_f32(z[o]);
     const float dx = dtv * xv;
-    float4* st = reinterpret_cast<float4*>(state + o * NS);
+    const int64_t so = (rows ? (int64_t)rows[m] : (int64_t)m) * d_inner + d;
+    float4* st = reinterpret_cast<float4*>(state + so * NS);
     float h[NS];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -316,10 +319,11 @@ size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int bat
 }
 
 hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
-                              const bf16* conv_b, bf16* conv_state, bf16* xh, bf16* z, int M,
-                              int d_model, int d_inner, hipStream_t s) {
+                              const bf16* conv_b, bf16* conv_state, const int32_t* rows,
+                              bf16* xh, bf16* z, int M, int d_model, int d_inner, hipStream_t s) {
   DecEpiArgs e = {};
-  e.xh = xh; e.z = z; e.conv_state = conv_state; e.conv_w = conv_w; e.conv_b = conv_b;
+  e.xh = xh; e.z = z; e.conv_state = conv_state; e.rows = rows; e.conv_w = conv_w;
+  e.conv_b = conv_b;
   e.d_inner = d_inner;
   return launch_dec_gemm<4, 2, DEC_INPROJ_CONV>(u, W_in, M, 2 * d_inner, d_model, 1, e, s);
 }
@@ -340,11 +344,12 @@ hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf
 
 hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, const float* Bm,
                              const float* Cm, const bf16* W_dt, const float* b_dt,
-                             const float* A_log, const float* D, float* ssm_state, bf16* g, int M,
-                             int d_inner, int dt_rank, hipStream_t s) {
+                             const float* A_log, const float* D, float* ssm_state,
+                             const int32_t* rows, bf16* g, int M, int d_inner, int dt_rank,
+                             hipStream_t s) {
   hipLaunchKernelGGL(dec_update_kernel, dim3(d_inner / UPD_CH, (M + UPD_MT - 1) / UPD_MT),
                      dim3(256), 0, s, xh, z, delta, Bm,
-                     Cm, W_dt, b_dt, A_log, D, ssm_state, g, M, d_inner, dt_rank);
+                     Cm, W_dt, b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
   return hipGetLastError();
 }
 

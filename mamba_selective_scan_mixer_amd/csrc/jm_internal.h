@@ -77,38 +77,45 @@ hipError_t launch_gemm_f32(const float* X, int64_t ldx, const float* W, int64_t 
 
 template <typename T>
 hipError_t launch_conv_silu(const T* x, T* xh, const T* conv_w, const T* conv_b,
-                            const T* init_conv, const int32_t* cu, int n_seqs,
-                            int64_t n_tok, int d_inner, hipStream_t s);
+                            const T* init_conv, const int32_t* init_rows, const int32_t* cu,
+                            int n_seqs, int64_t n_tok, int d_inner, hipStream_t s);
 template <typename T>
-hipError_t launch_conv_final(const T* x, const T* init_conv, T* final_conv,
-                             const int32_t* cu, int n_seqs, int d_inner, hipStream_t s);
+hipError_t launch_conv_final(const T* x, const T* init_conv, const int32_t* init_rows,
+                             T* final_conv, const int32_t* final_rows, const int32_t* cu,
+                             int n_seqs, int d_inner, hipStream_t s);
 
 // Chunked selective scan: phase A (per-chunk end state and decay product),
 // phase B (carry across chunks), phase C (outputs g and final states).
 template <typename T>
 hipError_t launch_scan_chunk_state(const T* x, const float* dt, const float* A_log,
-                                   const float* Bm, const float* init, const int32_t* cu,
-                                   float* agg_P, float* agg_h, int n_seqs, int64_t n_tok,
-                                   int d_inner, int chunk_len, int n_chunks, hipStream_t s);
+                                   const float* Bm, const float* init, const int32_t* init_rows,
+                                   const int32_t* cu, float* agg_P, float* agg_h, int n_seqs,
+                                   int64_t n_tok, int d_inner, int chunk_len, int n_chunks,
+                                   hipStream_t s);
 hipError_t launch_scan_chunk_carry(const float* agg_P, const float* agg_h, float* carry,
                                    int d_inner, int n_chunks, hipStream_t s);
 template <typename T>
 hipError_t launch_scan_chunk_output(const T* x, const float* dt, const float* A_log,
                                     const float* Bm, const float* Cm, const float* D, const T* z,
-                                    T* g, const float* init, float* final_state,
-                                    const float* carry, const int32_t* cu, int n_seqs,
-                                    int64_t n_tok, int d_inner, int chunk_len, int n_chunks,
-                                    hipStream_t s);
+                                    T* g, const float* init, const int32_t* init_rows,
+                                    float* final_state, const float* carry, const int32_t* cu,
+                                    int n_seqs, int64_t n_tok, int d_inner, int chunk_len,
+                                    int n_chunks, hipStream_t s);
+// Copy row i of src to row rows[i] of dst (rows[i] >= 0), row_floats floats per row.
+hipError_t launch_scatter_rows(const float* src, float* dst, const int32_t* rows, int n_rows,
+                               int64_t row_floats, hipStream_t s);
 
 // Decode (one token per sequence).
 template <typename T>
-hipError_t launch_decode_conv(const T* x, T* xh, T* conv_state, const T* conv_w,
-                              const T* conv_b, int batch, int d_inner, hipStream_t s);
+hipError_t launch_decode_conv(const T* x, T* xh, T* conv_state, const int32_t* rows,
+                              const T* conv_w, const T* conv_b, int batch, int d_inner,
+                              hipStream_t s);
 template <typename T>
 hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const float* Bm,
                                 const float* Cm, const T* W_dt, const float* b_dt,
-                                const float* A_log, const float* D, float* ssm_state, T* g,
-                                int batch, int d_inner, int dt_rank, hipStream_t s);
+                                const float* A_log, const float* D, float* ssm_state,
+                                const int32_t* rows, T* g, int batch, int d_inner, int dt_rank,
+                                hipStream_t s);
 
 // Inner RMSNorm (optional), in place, row by row: delta (M, R) act dtype, B and C (M, 16)
 // fp32, each v <- v / sqrt(mean(v^2) + eps) * gain.
@@ -120,15 +127,17 @@ hipError_t launch_inner_rmsnorm(T* delta, float* Bm, float* Cm, const float* g_d
 // Decode fast path (bf16; d_model % 256, d_inner % 1024, dt_rank % 128; <= 64 rows per launch).
 bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank);
 size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile);
+// rows: state row (slot) of each token row, or NULL for row m = token row m.
 hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
-                              const bf16* conv_b, bf16* conv_state, bf16* xh, bf16* z, int M,
-                              int d_model, int d_inner, hipStream_t s);
+                              const bf16* conv_b, bf16* conv_state, const int32_t* rows,
+                              bf16* xh, bf16* z, int M, int d_model, int d_inner, hipStream_t s);
 hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf16* delta,
                              float* Bm, float* Cm, int M, int d_inner, int dt_rank, hipStream_t s);
 hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, const float* Bm,
                              const float* Cm, const bf16* W_dt, const float* b_dt,
-                             const float* A_log, const float* D, float* ssm_state, bf16* g, int M,
-                             int d_inner, int dt_rank, hipStream_t s);
+                             const float* A_log, const float* D, float* ssm_state,
+                             const int32_t* rows, bf16* g, int M, int d_inner, int dt_rank,
+                             hipStream_t s);
 hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, bf16* out, int M,
                                int d_model, int d_inner, hipStream_t s);
 

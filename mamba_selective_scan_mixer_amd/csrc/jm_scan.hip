@@ -54,9 +54,11 @@ template <typename T>
 __global__ __launch_bounds__(256)
 void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                              const float* __restrict__ A_log, const float* __restrict__ Bm,
-                             const float* __restrict__ init, const int32_t* __restrict__ cu,
-                             float* __restrict__ agg_P, float* __restrict__ agg_h,
-                             int n_seqs, int64_t n_tok, int d_inner, int chunk_len) {
+                             const float* __restrict__ init,
+                             const int32_t* __restrict__ init_rows,
+                             const int32_t* __restrict__ cu, float* __restrict__ agg_P,
+                             float* __restrict__ agg_h, int n_seqs, int64_t n_tok, int d_inner,
+                             int chunk_len) {
   const int d = blockIdx.x * blockDim.x + threadIdx.x;
   const int k = blockIdx.y;
   const int64_t t0 = (int64_t)k * chunk_len;
@@ -74,7 +76,8 @@ void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ 
     if (s_begin == t) {
       reset = true;
       dsum = 0.0f;
-      if (init) load16(init + ((int64_t)i * d_inner + d) * NS, h);
+      const int64_t r = init_rows ? (int64_t)init_rows[i] : (int64_t)i;   // -1: zeros
+      if (init && r >= 0) load16(init + (r * d_inner + d) * NS, h);
       else
 #pragma unroll
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
@@ -134,9 +137,11 @@ void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__
                               const float* __restrict__ A_log, const float* __restrict__ Bm,
                               const float* __restrict__ Cm, const float* __restrict__ Dv,
                               const T* __restrict__ z, T* __restrict__ g,
-                              const float* __restrict__ init, float* __restrict__ final_state,
-                              const float* __restrict__ carry, const int32_t* __restrict__ cu,
-                              int n_seqs, int64_t n_tok, int d_inner, int chunk_len) {
+                              const float* __restrict__ init,
+                              const int32_t* __restrict__ init_rows,
+                              float* __restrict__ final_state, const float* __restrict__ carry,
+                              const int32_t* __restrict__ cu, int n_seqs, int64_t n_tok,
+                              int d_inner, int chunk_len) {
   const int d = blockIdx.x * blockDim.x + threadIdx.x;
   const int k = blockIdx.y;
   const int64_t t0 = (int64_t)k * chunk_len;
@@ -153,7 +158,8 @@ void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__
   while (t < t1) {
     const int64_t s_begin = cu[i], s_end = cu[i + 1];
     if (s_begin == t) {
-      if (init) load16(init + ((int64_t)i * d_inner + d) * NS, h);
+      const int64_t r = init_rows ? (int64_t)init_rows[i] : (int64_t)i;   // -1: zeros
+      if (init && r >= 0) load16(init + (r * d_inner + d) * NS, h);
       else
 #pragma unroll
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
@@ -202,7 +208,8 @@ void decode_update_kernel(const T* __restrict__ xh, const T* __restrict__ z,
                           const float* __restrict__ Cm, const T* __restrict__ W_dt,
                           const float* __restrict__ b_dt, const float* __restrict__ A_log,
                           const float* __restrict__ Dv, float* __restrict__ state,
-                          T* __restrict__ g, int d_inner, int dt_rank) {
+                          const int32_t* __restrict__ rows, T* __restrict__ g, int d_inner,
+                          int dt_rank) {
   const int d = blockIdx.x * blockDim.x + threadIdx.x;
   const int bi = blockIdx.y;
   if (d >= d_inner) return;
@@ -217,7 +224,7 @@ void decode_update_kernel(const T* __restrict__ xh, const T* __restrict__ z,
   const float dx = dtv * xv;
   float a2[NS], h[NS];
   load_a2(A_log, d, a2);
-  float* st = state + o * NS;
+  float* st = state + ((rows ? (int64_t)rows[bi] : (int64_t)bi) * d_inner + d) * NS;
   load16(st, h);
   const float* b = Bm + (int64_t)bi * NS;
   const float* c = Cm + (int64_t)bi * NS;
@@ -232,20 +239,33 @@ void decode_update_kernel(const T* __restrict__ xh, const T* __restrict__ z,
   g[o] = from_f32<T>(y * silu(zv));
 }
 
+// Copy row i of src (row_floats values) to row rows[i] of dst, for rows[i] >= 0.
+__global__ __launch_bounds__(256)
+void scatter_rows_kernel(const float* __restrict__ src, float* __restrict__ dst,
+                         const int32_t* __restrict__ rows, int64_t row_floats) {
+  const int i = blockIdx.y;
+  const int64_t r = rows[i];
+  if (r < 0) return;
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < row_floats;
+       j += (int64_t)gridDim.x * 256)
+    dst[r * row_floats + j] = src[(int64_t)i * row_floats + j];
+}
+
 inline int scan_block(int d_inner) { return d_inner % 256 == 0 ? 256 : (d_inner % 128 == 0 ? 128 : 64); }
 
 }  // namespace
 
 template <typename T>
 hipError_t launch_scan_chunk_state(const T* x, const float* dt, const float* A_log,
-                                   const float* Bm, const float* init, const int32_t* cu,
+                                   const float* Bm, const float* init, const int32_t* init_rows,
+                                   const int32_t* cu,
                                    float* agg_P, float* agg_h, int n_seqs, int64_t n_tok,
                                    int d_inner, int chunk_len, int n_chunks, hipStream_t s) {
   if (n_chunks <= 0) return hipSuccess;
   const int block = scan_block(d_inner);
   dim3 grid(d_inner / block, n_chunks);
   hipLaunchKernelGGL(scan_chunk_state_kernel<T>, grid, dim3(block), 0, s, x, dt, A_log, Bm, init,
-                     cu, agg_P, agg_h, n_seqs, n_tok, d_inner, chunk_len);
+                     init_rows, cu, agg_P, agg_h, n_seqs, n_tok, d_inner, chunk_len);
   return hipGetLastError();
 }
 
@@ -260,43 +280,55 @@ hipError_t launch_scan_chunk_carry(const float* agg_P, const float* agg_h, float
 template <typename T>
 hipError_t launch_scan_chunk_output(const T* x, const float* dt, const float* A_log,
                                     const float* Bm, const float* Cm, const float* D, const T* z,
-                                    T* g, const float* init, float* final_state,
-                                    const float* carry, const int32_t* cu, int n_seqs,
+                                    T* g, const float* init, const int32_t* init_rows,
+                                    float* final_state, const float* carry, const int32_t* cu,
+                                    int n_seqs,
                                     int64_t n_tok, int d_inner, int chunk_len, int n_chunks,
                                     hipStream_t s) {
   const int block = scan_block(d_inner);
   dim3 grid(d_inner / block, n_chunks);
   hipLaunchKernelGGL(scan_chunk_output_kernel<T>, grid, dim3(block), 0, s, x, dt, A_log, Bm, Cm,
-                     D, z, g, init, final_state, carry, cu, n_seqs, n_tok, d_inner, chunk_len);
+                     D, z, g, init, init_rows, final_state, carry, cu, n_seqs, n_tok, d_inner,
+                     chunk_len);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const float* Bm,
                                 const float* Cm, const T* W_dt, const float* b_dt,
-                                const float* A_log, const float* D, float* ssm_state, T* g,
-                                int batch, int d_inner, int dt_rank, hipStream_t s) {
+                                const float* A_log, const float* D, float* ssm_state,
+                                const int32_t* rows, T* g, int batch, int d_inner, int dt_rank,
+                                hipStream_t s) {
   if (batch <= 0) return hipSuccess;
   dim3 grid((d_inner + 255) / 256, batch);
   hipLaunchKernelGGL(decode_update_kernel<T>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
-                     b_dt, A_log, D, ssm_state, g, d_inner, dt_rank);
+                     b_dt, A_log, D, ssm_state, rows, g, d_inner, dt_rank);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const float* src, float* dst, const int32_t* rows, int n_rows,
+                               int64_t row_floats, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  const int64_t bx = (row_floats + 255) / 256 < 64 ? (row_floats + 255) / 256 : 64;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)bx, n_rows), dim3(256), 0, s, src, dst,
+                     rows, row_floats);
   return hipGetLastError();
 }
 
 #define JM_INST_SCAN(T)                                                                          \
   template hipError_t launch_scan_chunk_state<T>(const T*, const float*, const float*,          \
                                                  const float*, const float*, const int32_t*,    \
-                                                 float*, float*, int, int64_t, int, int, int,   \
-                                                 hipStream_t);                                  \
+                                                 const int32_t*, float*, float*, int, int64_t,  \
+                                                 int, int, int, hipStream_t);                   \
   template hipError_t launch_scan_chunk_output<T>(const T*, const float*, const float*,         \
                                                   const float*, const float*, const float*,     \
-                                                  const T*, T*, const float*, float*,           \
-                                                  const float*, const int32_t*, int, int64_t,   \
-                                                  int, int, int, hipStream_t);                  \
+                                                  const T*, T*, const float*, const int32_t*,   \
+                                                  float*, const float*, const int32_t*, int,    \
+                                                  int64_t, int, int, int, hipStream_t);         \
   template hipError_t launch_decode_update<T>(const T*, const T*, const T*, const float*,        \
                                               const float*, const T*, const float*,             \
-                                              const float*, const float*, float*, T*, int, int, \
-                                              int, hipStream_t);
+                                              const float*, const float*, float*,               \
+                                              const int32_t*, T*, int, int, int, hipStream_t);
 JM_INST_SCAN(float)
 JM_INST_SCAN(bf16)
 #undef JM_INST_SCAN

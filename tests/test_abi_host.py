@@ -205,6 +205,44 @@ def test_stage_validation_paths(L):
     assert L.jm_stage_scan(*args(None, None, f(), need.value, h=bad, n=2, T=9)) == S["JM_ERR_SHAPE"]
 
 
+def test_state_cache_validation_paths(L):
+    """Slot arrays of the state-cache entry points are checked on the host."""
+    f = _Fake()
+    d = dims()
+    w = _weights(f)
+    S = {n: i for i, n in enumerate(jm._STATUS)}
+    D, W = ctypes.byref(d), ctypes.byref(w)
+    cu = [0, 5, 9, 10]
+    host = (ctypes.c_int32 * 4)(*cu)
+    arr = lambda *v: (ctypes.c_int32 * len(v))(*v)  # noqa: E731
+    need = jm.prefill_slots_workspace_size(d, 3, 10)
+    assert need > jm.prefill_workspace_size(d, 3, 10)
+
+    def pre(init, fin, n_slots=8, init_dev=True, fin_dev=True, nb=need):
+        return L.jamba_mamba_prefill_slots(
+            D, W, f(), f(), host, 3, 10, f() if (init is not None and init_dev) else None, init,
+            f() if (fin is not None and fin_dev) else None, fin, f(), f(), n_slots, f(), f(), nb,
+            None)
+
+    assert pre(arr(0, 1, 8), arr(0, 1, 2)) == S["JM_ERR_SHAPE"]           # slot 8 of 8
+    assert pre(arr(0, -2, 1), None) == S["JM_ERR_SHAPE"]                  # below -1
+    assert pre(None, arr(3, 4, 3)) == S["JM_ERR_INVALID_ARG"]             # final slot twice
+    assert pre(arr(3, -1, -1), arr(4, 3, -1)) == S["JM_ERR_INVALID_ARG"]  # another's init slot
+    assert pre(arr(3, 4, 5), arr(3, 4, 5), init_dev=False) == S["JM_ERR_INVALID_ARG"]
+    assert pre(arr(3, 4, 5), arr(3, 4, 5), n_slots=0) == S["JM_ERR_INVALID_ARG"]
+    assert pre(arr(3, 4, 5), arr(3, 4, 5), nb=need - 1) == S["JM_ERR_WORKSPACE"]
+    dneed = jm.decode_workspace_size(d, 3)
+
+    def dec(slots, n_slots=8, dev=True):
+        return L.jamba_mamba_decode_step_slots(D, W, f(), 3, f() if dev else None, slots, f(),
+                                               f(), n_slots, f(), f(), dneed, None)
+
+    assert dec(arr(0, 8, 1)) == S["JM_ERR_SHAPE"]
+    assert dec(arr(0, -1, 1)) == S["JM_ERR_SHAPE"]
+    assert dec(arr(2, 5, 2)) == S["JM_ERR_INVALID_ARG"]
+    assert dec(arr(2, 5, 3), dev=False) == S["JM_ERR_INVALID_ARG"]
+
+
 def expected_segments(cu, chunk_len):
     """Independent statement of the chunking: chunk c covers [c*L, min((c+1)*L, T))."""
     T = cu[-1]

@@ -10,7 +10,7 @@
 // Main bf16 kernel (K % 32 == 0):
 //   * 256 x 256 macro tile, 512 threads = 8 waves (two per SIMD, so one wave's
 //     waits and address arithmetic overlap the other's MFMAs), wave tile 64 x 128;
-//   * operands go global -> LDS directly (global_load_lds_dwordx4, no VGPR
+//   * operands go global -> LDS directly (buffer_load_dwordx4 ... lds, no VGPR
 //     staging) through a 4-stage ring of 32-deep K slices, so loads run ~2.5
 //     stages ahead of the matrix cores; waits are explicit vmcnt counts;
 //   * LDS rows are 32 bf16 = 4 chunks of 16 bytes; chunk c of row r sits at
@@ -237,6 +237,10 @@ void gemm_bf16_regstage_kernel(const bf16* __restrict__ X, int64_t ldx,
 // ---- main bf16 kernel: multi-stage direct-to-LDS ring ----------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Fourth word of a raw buffer descriptor on gfx9-family GPUs (32-bit data format; no swizzle,
+// no index stride).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // Chunk position of 16-byte chunk 0 of row r in a 32-column (64-byte) LDS row.
 __device__ __forceinline__ int swz32(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
@@ -282,36 +286,46 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // Each DMA instruction fills 1 KB of LDS: lane l writes slot l, i.e. row l / CPR,
   // chunk position l % CPR, so it loads the global chunk that belongs there.
   // Rows past M / N are clamped to the last row (their results are never stored).
-  const bf16* xsrc[XI];
-  const bf16* wsrc[WI];
+  // The loads are buffer loads: one descriptor per operand whose base is the tile's first
+  // row, a fixed 32-bit byte offset per lane and instruction, and the k advance in the
+  // scalar offset (the host checks that 256 rows + K fit 2^31 bytes). Their per-lane
+  // address is half the size of a global load's, which measured ~2% faster here.
+  uint32_t xoff[XI], woff[WI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int row = (wave * XI + i) * RPI + lane / CPR;
     const int c = (lane % CPR) ^ swz32(row);
-    int64_t grow = m0 + row;
-    if (grow >= M) grow = M - 1;
-    xsrc[i] = X + grow * ldx + c * 8;
+    int64_t r = row;
+    if (m0 + r >= M) r = M - 1 - m0;
+    xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
   }
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int row = (wave * WI + i) * RPI + lane / CPR;
     const int c = (lane % CPR) ^ swz32(row);
-    int grow = n0 + row;
-    if (grow >= N) grow = N - 1;
-    wsrc[i] = W + (int64_t)grow * ldw + c * 8;
+    int64_t r = row;
+    if (n0 + r >= N) r = N - 1 - n0;
+    woff[i] = (uint32_t)((r * ldw + c * 8) * 2);
   }
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + m0 * ldx), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * ldw), (short)0, 0x7fffffff, kBufferRsrcWord3);
+#endif
   auto issue = [&](int kt, int buf) {
-    const int k0 = kt * BKC;
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int kb = kt * BKC * 2;
     char* base = reinterpret_cast<char*>(lds + buf * STAGE);
 #pragma unroll
     for (int i = 0; i < XI; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[i] + k0),
-                                       (lds_void*)(base + (wave * XI + i) * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(base + (wave * XI + i) * 1024), 16,
+                                               xoff[i], kb, 0, 0);
 #pragma unroll
     for (int i = 0; i < WI; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + k0),
-                                       (lds_void*)(base + BM * BKC * 2 + (wave * WI + i) * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (lds_void*)(base + BM * BKC * 2 + (wave * WI + i) * 1024), 16, woff[i], kb, 0, 0);
+#endif
   };
   const int lrow = lane & 31;
   const int khalf = lane >> 5;
@@ -562,7 +576,10 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
                          epi.bias, epi.outf0);
     return hipGetLastError();
   }
-  if (K % MS_BK == 0) {
+  // buffer-load offsets (256 rows + K, in bytes) must fit 31 bits
+  const bool offsets_fit = ((int64_t)MS_BM * ldx + K) * 2 < ((int64_t)1 << 31) &&
+                           ((int64_t)MS_BN * ldw + K) * 2 < ((int64_t)1 << 31);
+  if (K % MS_BK == 0 && offsets_fit) {
     const int64_t tiles_m = (M + MS_BM - 1) / MS_BM;
     const int tiles_n = (N + MS_BN - 1) / MS_BN;
     const int64_t n_wg = tiles_m * tiles_n;

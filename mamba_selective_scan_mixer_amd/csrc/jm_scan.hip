@@ -50,7 +50,9 @@ __device__ __forceinline__ void store16(float* __restrict__ p, const float v[NS]
     reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-template <typename T>
+// ROWS: whether initial states go through a slot map (init_rows); a compile-time choice so
+// the plain path keeps its register allocation and schedule.
+template <typename T, bool ROWS>
 __global__ __launch_bounds__(256)
 void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                              const float* __restrict__ A_log, const float* __restrict__ Bm,
@@ -76,7 +78,7 @@ void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ 
     if (s_begin == t) {
       reset = true;
       dsum = 0.0f;
-      const int64_t r = init_rows ? (int64_t)init_rows[i] : (int64_t)i;   // -1: zeros
+      const int64_t r = ROWS ? (int64_t)init_rows[i] : (int64_t)i;   // -1: zeros
       if (init && r >= 0) load16(init + (r * d_inner + d) * NS, h);
       else
 #pragma unroll
@@ -131,7 +133,7 @@ void scan_chunk_carry_kernel(const float* __restrict__ agg_P, const float* __res
   }
 }
 
-template <typename T>
+template <typename T, bool ROWS>
 __global__ __launch_bounds__(256)
 void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                               const float* __restrict__ A_log, const float* __restrict__ Bm,
@@ -158,7 +160,7 @@ void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__
   while (t < t1) {
     const int64_t s_begin = cu[i], s_end = cu[i + 1];
     if (s_begin == t) {
-      const int64_t r = init_rows ? (int64_t)init_rows[i] : (int64_t)i;   // -1: zeros
+      const int64_t r = ROWS ? (int64_t)init_rows[i] : (int64_t)i;   // -1: zeros
       if (init && r >= 0) load16(init + (r * d_inner + d) * NS, h);
       else
 #pragma unroll
@@ -264,8 +266,12 @@ hipError_t launch_scan_chunk_state(const T* x, const float* dt, const float* A_l
   if (n_chunks <= 0) return hipSuccess;
   const int block = scan_block(d_inner);
   dim3 grid(d_inner / block, n_chunks);
-  hipLaunchKernelGGL(scan_chunk_state_kernel<T>, grid, dim3(block), 0, s, x, dt, A_log, Bm, init,
-                     init_rows, cu, agg_P, agg_h, n_seqs, n_tok, d_inner, chunk_len);
+  if (init_rows)
+    hipLaunchKernelGGL((scan_chunk_state_kernel<T, true>), grid, dim3(block), 0, s, x, dt, A_log,
+                       Bm, init, init_rows, cu, agg_P, agg_h, n_seqs, n_tok, d_inner, chunk_len);
+  else
+    hipLaunchKernelGGL((scan_chunk_state_kernel<T, false>), grid, dim3(block), 0, s, x, dt, A_log,
+                       Bm, init, init_rows, cu, agg_P, agg_h, n_seqs, n_tok, d_inner, chunk_len);
   return hipGetLastError();
 }
 
@@ -287,9 +293,14 @@ hipError_t launch_scan_chunk_output(const T* x, const float* dt, const float* A_
                                     hipStream_t s) {
   const int block = scan_block(d_inner);
   dim3 grid(d_inner / block, n_chunks);
-  hipLaunchKernelGGL(scan_chunk_output_kernel<T>, grid, dim3(block), 0, s, x, dt, A_log, Bm, Cm,
-                     D, z, g, init, init_rows, final_state, carry, cu, n_seqs, n_tok, d_inner,
-                     chunk_len);
+  if (init_rows)
+    hipLaunchKernelGGL((scan_chunk_output_kernel<T, true>), grid, dim3(block), 0, s, x, dt, A_log,
+                       Bm, Cm, D, z, g, init, init_rows, final_state, carry, cu, n_seqs, n_tok,
+                       d_inner, chunk_len);
+  else
+    hipLaunchKernelGGL((scan_chunk_output_kernel<T, false>), grid, dim3(block), 0, s, x, dt, A_log,
+                       Bm, Cm, D, z, g, init, init_rows, final_state, carry, cu, n_seqs, n_tok,
+                       d_inner, chunk_len);
   return hipGetLastError();
 }
 

@@ -277,6 +277,29 @@ jm_status jm_stage_scan(const jm_layer_dims *dims, const jm_layer_weights *weigh
 jm_status jm_stage_out_proj(const jm_layer_dims *dims, const jm_layer_weights *weights,
                             const void *g, int64_t total_tokens, void *out, void *stream);
 
+/* ---- Backward of the scan step (training) ----------------------------------------------
+ * Gradients of jm_stage_scan's output (g = (scan(x_hat, Delta, A, B, C; h0) + D x_hat) *
+ * SiLU(z), per sequence of cu_seqlens) for the training step (Jamba paper §3.1: trained up to
+ * 1M-token contexts; §6.4 on training stability), by reverse mode through the recurrence.
+ * Inputs as jm_stage_scan's (x_hat, z act dtype; dt, B, C fp32; init_ssm_state fp32 or NULL),
+ * plus dg (T, d_inner) act dtype = dL/dg and d_final_ssm_state (n_seqs, d_inner, d_state)
+ * fp32 or NULL = dL/d(final state). Outputs, all fp32 and fully overwritten: dx_hat, ddt, dz
+ * (T, d_inner); dB, dC (T, d_state); dA_log (d_inner, d_state); dD (d_inner); and
+ * d_init_ssm_state (n_seqs, d_inner, d_state) or NULL. A_log and D are read from weights.
+ * Deterministic (fixed-order reductions). workspace >= jm_scan_backward_workspace_size.
+ */
+jm_status jm_scan_backward_workspace_size(const jm_layer_dims *dims, int64_t total_tokens,
+                                          size_t *bytes);
+jm_status jamba_mamba_scan_backward(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                                    const void *x_hat, const float *dt, const float *B,
+                                    const float *C, const void *z, const void *dg,
+                                    const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                    int32_t n_seqs, int64_t total_tokens,
+                                    const float *init_ssm_state, const float *d_final_ssm_state,
+                                    float *dx_hat, float *ddt, float *dB, float *dC, float *dz,
+                                    float *dA_log, float *dD, float *d_init_ssm_state,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- Kernel timing (diagnostics; the benchmark reads per-kernel durations) ----
  * While enabled, every kernel the library enqueues is bracketed by a pair of HIP
  * events on the caller's stream. jm_profile_read synchronises those events and

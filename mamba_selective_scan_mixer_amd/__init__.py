@@ -111,6 +111,11 @@ def lib() -> ctypes.CDLL:
         L.jamba_mamba_prefill_slots.argtypes = [
             D, W, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P,
             ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+        L.jm_scan_backward_workspace_size.argtypes = [D, ctypes.c_int64,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+        L.jamba_mamba_scan_backward.argtypes = [
+            D, W, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
+            _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.jamba_mamba_decode_step_slots.argtypes = [
             D, W, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
         for name in ("jm_prefill_workspace_size", "jm_decode_workspace_size", "jamba_mamba_prefill",
@@ -119,7 +124,8 @@ def lib() -> ctypes.CDLL:
                      "jm_stage_in_proj", "jm_stage_conv", "jm_stage_x_proj", "jm_stage_dt_proj",
                      "jm_stage_scan_workspace_size", "jm_stage_scan", "jm_stage_out_proj",
                      "jm_prefill_slots_workspace_size", "jamba_mamba_prefill_slots",
-                     "jamba_mamba_decode_step_slots"):
+                     "jamba_mamba_decode_step_slots", "jm_scan_backward_workspace_size",
+                     "jamba_mamba_scan_backward"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -516,4 +522,52 @@ def jamba_mamba_decode_step_slots(layer: MambaLayer, u: torch.Tensor, cache: Sta
         ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), b, _ptr(slots_device), host,
         _ptr(cache.conv), _ptr(cache.ssm), cache.n_slots, _ptr(out), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+    return out
+
+
+# ---- backward of the scan step (training) ----------------------------------------------------
+
+def jm_scan_backward_workspace_size(dims: LayerDims, total_tokens: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().jm_scan_backward_workspace_size(ctypes.byref(dims), total_tokens,
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def jamba_mamba_scan_backward(layer: MambaLayer, x_hat: torch.Tensor, dt: torch.Tensor,
+                              B: torch.Tensor, C: torch.Tensor, z: torch.Tensor, dg: torch.Tensor,
+                              cu_seqlens: torch.Tensor, cu_seqlens_host: Sequence[int],
+                              init_ssm_state=None, d_final_ssm_state=None, want_d_init=True,
+                              workspace=None, stream=None) -> Dict[str, torch.Tensor]:
+    """Gradients of the scan step's output g (see jm_stage_scan) given dg = dL/dg and
+    optionally dL/d(final state). Returns dict dx_hat, ddt, dz, dB, dC, dA_log, dD and
+    d_init_ssm_state (None unless want_d_init), all fp32."""
+    d, at = layer.dims, _torch_dtype(layer.dims)
+    host, n = _host_cu(cu_seqlens_host)
+    T = host[n]
+    di, N = d.d_inner, d.d_state
+    for name, t, dtp, shp in (("x_hat", x_hat, at, (T, di)), ("z", z, at, (T, di)),
+                              ("dg", dg, at, (T, di)), ("dt", dt, torch.float32, (T, di)),
+                              ("B", B, torch.float32, (T, N)), ("C", C, torch.float32, (T, N))):
+        _need(t, name, dtp, shp)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (n + 1,))
+    for name, t in (("init_ssm_state", init_ssm_state), ("d_final_ssm_state", d_final_ssm_state)):
+        if t is not None:
+            _need(t, name, torch.float32, (n, di, N))
+    dev = x_hat.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx_hat": torch.empty((T, di), **f32), "ddt": torch.empty((T, di), **f32),
+           "dz": torch.empty((T, di), **f32), "dB": torch.empty((T, N), **f32),
+           "dC": torch.empty((T, N), **f32), "dA_log": torch.empty((di, N), **f32),
+           "dD": torch.empty((di,), **f32),
+           "d_init_ssm_state": torch.empty((n, di, N), **f32) if want_d_init else None}
+    need = jm_scan_backward_workspace_size(d, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().jamba_mamba_scan_backward(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x_hat), _ptr(dt), _ptr(B), _ptr(C),
+        _ptr(z), _ptr(dg), _ptr(cu_seqlens), host, n, T, _ptr(init_ssm_state),
+        _ptr(d_final_ssm_state), _ptr(out["dx_hat"]), _ptr(out["ddt"]), _ptr(out["dB"]),
+        _ptr(out["dC"]), _ptr(out["dz"]), _ptr(out["dA_log"]), _ptr(out["dD"]),
+        _ptr(out["d_init_ssm_state"]), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

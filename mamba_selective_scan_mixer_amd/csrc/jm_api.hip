@@ -896,6 +896,60 @@ jm_status jm_stage_out_proj(const jm_layer_dims* dims, const jm_layer_weights* w
   return st == JM_OK ? ok() : st;
 }
 
+// ---- backward of the scan step (training) -------------------------------------------------
+jm_status jm_scan_backward_workspace_size(const jm_layer_dims* dims, int64_t total_tokens,
+                                          size_t* bytes) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if (!bytes) return fail(JM_ERR_INVALID_ARG, "bytes is NULL");
+  if (total_tokens < 0 || total_tokens >= ((int64_t)1 << 31))
+    return fail(JM_ERR_SHAPE, "total_tokens must be in [0, 2^31)");
+  *bytes = total_tokens == 0 ? 0
+                             : scan_backward_workspace_floats(total_tokens, dims->d_inner) * 4;
+  return ok();
+}
+
+jm_status jamba_mamba_scan_backward(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                                    const void* x_hat, const float* dt, const float* B,
+                                    const float* C, const void* z, const void* dg,
+                                    const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                                    int32_t n_seqs, int64_t total_tokens,
+                                    const float* init_ssm_state, const float* d_final_ssm_state,
+                                    float* dx_hat, float* ddt, float* dB, float* dC, float* dz,
+                                    float* dA_log, float* dD, float* d_init_ssm_state,
+                                    void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  jm_status st = check_stage(dims, weights, total_tokens);
+  if (st != JM_OK) return st;
+  if (n_seqs < 1) return fail(JM_ERR_SHAPE, "n_seqs must be >= 1");
+  if (!cu_seqlens) return fail(JM_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if ((st = check_cu(cu_seqlens_host, n_seqs, total_tokens)) != JM_OK) return st;
+  if ((st = check_ptrs({x_hat, dt, B, C, z, dg, dx_hat, ddt, dB, dC, dz, dA_log, dD, workspace},
+                       {init_ssm_state, d_final_ssm_state, d_init_ssm_state})) != JM_OK)
+    return st;
+  const size_t need = scan_backward_workspace_floats(total_tokens, dims->d_inner) * 4;
+  if (workspace_bytes < need)
+    return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  float* ws = static_cast<float*>(workspace);
+  if (dims->act_dtype == JM_BF16)
+    JM_LAUNCH("scan_backward",
+              launch_scan_backward<bf16>(static_cast<const bf16*>(x_hat), dt, weights->A_log, B, C,
+                                         weights->D, static_cast<const bf16*>(z),
+                                         static_cast<const bf16*>(dg), init_ssm_state,
+                                         d_final_ssm_state, cu_seqlens, n_seqs, total_tokens,
+                                         dims->d_inner, dx_hat, ddt, dz, dB, dC, dA_log, dD,
+                                         d_init_ssm_state, ws, stream));
+  else
+    JM_LAUNCH("scan_backward",
+              launch_scan_backward<float>(static_cast<const float*>(x_hat), dt, weights->A_log, B,
+                                          C, weights->D, static_cast<const float*>(z),
+                                          static_cast<const float*>(dg), init_ssm_state,
+                                          d_final_ssm_state, cu_seqlens, n_seqs, total_tokens,
+                                          dims->d_inner, dx_hat, ddt, dz, dB, dC, dA_log, dD,
+                                          d_init_ssm_state, ws, stream));
+  return ok();
+}
+
 jm_status jm_profile_enable(int32_t enable) {
   g_prof = enable != 0;
   return ok();

@@ -117,6 +117,17 @@ hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const f
                                 const int32_t* rows, T* g, int batch, int d_inner, int dt_rank,
                                 hipStream_t s);
 
+// Backward of the scan step (scan + D skip + gate) over packed sequences; all gradients
+// fp32. ws: scan_backward_workspace_floats(n_tok, d_inner) floats. d_inner % 64 == 0.
+size_t scan_backward_workspace_floats(int64_t n_tok, int d_inner);
+template <typename T>
+hipError_t launch_scan_backward(const T* x, const float* dt, const float* A_log, const float* Bm,
+                                const float* Cm, const float* D, const T* z, const T* dg,
+                                const float* h0, const float* dh_last, const int32_t* cu,
+                                int n_seqs, int64_t n_tok, int d_inner, float* dx, float* ddt,
+                                float* dz, float* dB, float* dC, float* dA_log, float* dD,
+                                float* dh0, float* ws, hipStream_t s);
+
 // Inner RMSNorm (optional), in place, row by row: delta (M, R) act dtype, B and C (M, 16)
 // fp32, each v <- v / sqrt(mean(v^2) + eps) * gain.
 template <typename T>

@@ -120,6 +120,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the scan-backward measurement")
     ap.add_argument("--no-inner-norm", action="store_true",
                     help="skip the prefill measurement with the inner RMSNorm on")
     ap.add_argument("--decode-steps", type=int, default=1024)
@@ -224,6 +226,12 @@ def main():
         print(f"[bench] prefill with inner norm {inner['ms_per_step']:.2f} ms/step "
               f"(norm kernel {inner['norm_kernel']['avg_ms']:.3f} ms)", file=sys.stderr, flush=True)
 
+    backward = None
+    if not args.no_backward:
+        backward = run_scan_backward(jm, torch, wl, layer, dims, u, cu, T)
+        print(f"[bench] scan backward {backward['ms_per_call']:.2f} ms/call "
+              f"({backward['tokens_per_s'] / 1e6:.3f} M tok/s)", file=sys.stderr, flush=True)
+
     decode = None
     if not args.no_decode:
         decode = run_decode(jm, torch, dev, layer, dims, wl, args.decode_steps)
@@ -249,9 +257,57 @@ def main():
         "cpu_baseline": cpu,
         "decode": decode,
         "inner_norm": inner,
+        "scan_backward": backward,
         "kernels": kernels,
     }
     print(json.dumps(rec), flush=True)
+
+
+def run_scan_backward(jm, torch, wl, layer, dims, u, cu, T, steps: int = 3):
+    """Backward of the scan step (training) over the same 131072-token sequence: inputs from
+    the stage entry points on the benchmark's tokens, a seeded N(0,1) upstream gradient dg."""
+    x, z = jm.jm_stage_in_proj(layer, u)
+    xh, _ = jm.jm_stage_conv(layer, x, cu, wl.cu_seqlens, want_final_state=False)
+    del x
+    delta, B, C = jm.jm_stage_x_proj(layer, xh)
+    dt = jm.jm_stage_dt_proj(layer, delta)
+    del delta
+    gen = torch.Generator(device=u.device)
+    gen.manual_seed(5)
+    dg = torch.randn(tuple(xh.shape), generator=gen, device=u.device).to(torch.bfloat16)
+    ws = torch.empty(jm.jm_scan_backward_workspace_size(dims, T), dtype=torch.uint8,
+                     device=u.device)
+
+    def call():
+        return jm.jamba_mamba_scan_backward(layer, xh, dt, B, C, z, dg, cu, wl.cu_seqlens,
+                                            want_d_init=False, workspace=ws)
+
+    g = call()
+    del g
+    torch.cuda.synchronize()
+    jm.profile_reset()
+    jm.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g = call()
+        del g
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    jm.profile_enable(False)
+    prof = jm.profile_read()
+    jm.profile_reset()
+    del xh, z, dt, dg, ws
+    torch.cuda.empty_cache()
+    di = dims.d_inner
+    # algorithmic bytes: inputs x_hat, z, dg (bf16), dt (fp32), B, C read once; dx, ddt, dz
+    # (fp32) written once; dB, dC written once
+    nbytes = T * di * (2 + 2 + 2 + 4 + 3 * 4) + T * 16 * 4 * 4
+    return {"ms_per_call": round(el * 1e3, 3), "tokens_per_s": round(T / el, 1), "steps": steps,
+            "algorithmic_bytes": nbytes,
+            "hbm_frac": round(nbytes / el / 1e9 / HBM_PEAK_GBS, 4),
+            "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in prof.items()},
+            "note": "gradients of the scan + D skip + gate step w.r.t. x_hat, Delta, B, C, z, "
+                    "A_log, D (fp32), 64-token chunks"}
 
 
 def run_inner_norm(jm, torch, wl, dims, u, cu, out, fconv, fssm, ws, T, steps: int = 5):

@@ -509,6 +509,33 @@ size_t slots_tmp_bytes(const jm_layer_dims& d, int32_t n_seqs) {
   return align256((size_t)n_seqs * d.d_inner * 16 * sizeof(float));
 }
 
+
+// ---- backward of the scan step: launch sequence ---------------------------------------------
+template <typename T>
+jm_status run_scan_backward(const jm_layer_dims& d, const jm_layer_weights& wt, const T* x,
+                            const float* dt, const float* B, const float* C, const T* z,
+                            const T* dg, const int32_t* cu, int32_t n_seqs, int64_t n_tok,
+                            const float* h0, const float* dh_last, float* dx, float* ddt,
+                            float* dB, float* dC, float* dz, float* dA_log, float* dD, float* dh0,
+                            const ScanBwdLayout& w, hipStream_t stream) {
+  const int di = d.d_inner;
+  if (w.K > 1) {
+    JM_LAUNCH("bwd_fwd_state", launch_scan_chunk_state<T>(x, dt, wt.A_log, B, h0, nullptr, cu,
+                                                          w.aggP, w.aggh, n_seqs, n_tok, di,
+                                                          w.chunk, w.K - 1, stream));
+    JM_LAUNCH("bwd_fwd_carry", launch_scan_chunk_carry(w.aggP, w.aggh, w.carry, di, w.K, stream));
+    JM_LAUNCH("bwd_adjoint", launch_scan_bwd_adjoint<T>(dg, z, dt, wt.A_log, C, dh_last, cu, w,
+                                                        n_seqs, n_tok, di, stream));
+    JM_LAUNCH("bwd_carry", launch_scan_bwd_carry(w, di, stream));
+  }
+  JM_LAUNCH("bwd_main", launch_scan_bwd_main<T>(x, dt, wt.A_log, B, C, wt.D, z, dg, h0, dh_last,
+                                                cu, w, n_seqs, n_tok, di, dx, ddt, dz, dh0,
+                                                stream));
+  JM_LAUNCH("bwd_reduce", launch_scan_bwd_reduce(w, wt.A_log, n_tok, di, dB, dC, dA_log, dD,
+                                                 stream));
+  return JM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -930,24 +957,21 @@ jm_status jamba_mamba_scan_backward(const jm_layer_dims* dims, const jm_layer_we
   if (workspace_bytes < need)
     return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-  float* ws = static_cast<float*>(workspace);
+  const ScanBwdLayout w = scan_backward_layout(static_cast<float*>(workspace), total_tokens,
+                                               dims->d_inner);
   if (dims->act_dtype == JM_BF16)
-    JM_LAUNCH("scan_backward",
-              launch_scan_backward<bf16>(static_cast<const bf16*>(x_hat), dt, weights->A_log, B, C,
-                                         weights->D, static_cast<const bf16*>(z),
-                                         static_cast<const bf16*>(dg), init_ssm_state,
-                                         d_final_ssm_state, cu_seqlens, n_seqs, total_tokens,
-                                         dims->d_inner, dx_hat, ddt, dz, dB, dC, dA_log, dD,
-                                         d_init_ssm_state, ws, stream));
+    st = run_scan_backward<bf16>(*dims, *weights, static_cast<const bf16*>(x_hat), dt, B, C,
+                                 static_cast<const bf16*>(z), static_cast<const bf16*>(dg),
+                                 cu_seqlens, n_seqs, total_tokens, init_ssm_state,
+                                 d_final_ssm_state, dx_hat, ddt, dB, dC, dz, dA_log, dD,
+                                 d_init_ssm_state, w, stream);
   else
-    JM_LAUNCH("scan_backward",
-              launch_scan_backward<float>(static_cast<const float*>(x_hat), dt, weights->A_log, B,
-                                          C, weights->D, static_cast<const float*>(z),
-                                          static_cast<const float*>(dg), init_ssm_state,
-                                          d_final_ssm_state, cu_seqlens, n_seqs, total_tokens,
-                                          dims->d_inner, dx_hat, ddt, dz, dB, dC, dA_log, dD,
-                                          d_init_ssm_state, ws, stream));
-  return ok();
+    st = run_scan_backward<float>(*dims, *weights, static_cast<const float*>(x_hat), dt, B, C,
+                                  static_cast<const float*>(z), static_cast<const float*>(dg),
+                                  cu_seqlens, n_seqs, total_tokens, init_ssm_state,
+                                  d_final_ssm_state, dx_hat, ddt, dB, dC, dz, dA_log, dD,
+                                  d_init_ssm_state, w, stream);
+  return st == JM_OK ? ok() : st;
 }
 
 jm_status jm_profile_enable(int32_t enable) {

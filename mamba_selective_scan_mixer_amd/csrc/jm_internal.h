@@ -118,15 +118,30 @@ hipError_t launch_decode_update(const T* xh, const T* z, const T* delta, const f
                                 hipStream_t s);
 
 // Backward of the scan step (scan + D skip + gate) over packed sequences; all gradients
-// fp32. ws: scan_backward_workspace_floats(n_tok, d_inner) floats. d_inner % 64 == 0.
+// fp32; d_inner % 64 == 0. Workspace: scan_backward_workspace_floats floats, carved by
+// scan_backward_layout. Order: forward chunk states (launch_scan_chunk_state / _carry at
+// chunk length layout.chunk), adjoint, carry, main, reduce.
+struct ScanBwdLayout {
+  int K, chunk;
+  float *aggP, *aggh, *carry, *L, *Iin, *dA_part, *dD_part, *bc_part;
+};
 size_t scan_backward_workspace_floats(int64_t n_tok, int d_inner);
+ScanBwdLayout scan_backward_layout(float* ws, int64_t n_tok, int d_inner);
 template <typename T>
-hipError_t launch_scan_backward(const T* x, const float* dt, const float* A_log, const float* Bm,
+hipError_t launch_scan_bwd_adjoint(const T* dg, const T* z, const float* dt, const float* A_log,
+                                   const float* Cm, const float* dh_last, const int32_t* cu,
+                                   const ScanBwdLayout& w, int n_seqs, int64_t n_tok, int d_inner,
+                                   hipStream_t s);
+hipError_t launch_scan_bwd_carry(const ScanBwdLayout& w, int d_inner, hipStream_t s);
+template <typename T>
+hipError_t launch_scan_bwd_main(const T* x, const float* dt, const float* A_log, const float* Bm,
                                 const float* Cm, const float* D, const T* z, const T* dg,
                                 const float* h0, const float* dh_last, const int32_t* cu,
-                                int n_seqs, int64_t n_tok, int d_inner, float* dx, float* ddt,
-                                float* dz, float* dB, float* dC, float* dA_log, float* dD,
-                                float* dh0, float* ws, hipStream_t s);
+                                const ScanBwdLayout& w, int n_seqs, int64_t n_tok, int d_inner,
+                                float* dx, float* ddt, float* dz, float* dh0, hipStream_t s);
+hipError_t launch_scan_bwd_reduce(const ScanBwdLayout& w, const float* A_log, int64_t n_tok,
+                                  int d_inner, float* dB, float* dC, float* dA_log, float* dD,
+                                  hipStream_t s);
 
 // Inner RMSNorm (optional), in place, row by row: delta (M, R) act dtype, B and C (M, 16)
 // fp32, each v <- v / sqrt(mean(v^2) + eps) * gain.

@@ -371,67 +371,78 @@ size_t scan_backward_workspace_floats(int64_t n_tok, int d_inner) {
   return (size_t)(6 * K * dn + K * d_inner + ncb * n_tok * 2 * NS);
 }
 
-template <typename T>
-hipError_t launch_scan_backward(const T* x, const float* dt, const float* A_log, const float* Bm,
-                                const float* Cm, const float* D, const T* z, const T* dg,
-                                const float* h0, const float* dh_last, const int32_t* cu,
-                                int n_seqs, int64_t n_tok, int d_inner, float* dx, float* ddt,
-                                float* dz, float* dB, float* dC, float* dA_log, float* dD,
-                                float* dh0, float* ws, hipStream_t s) {
-  if (n_tok <= 0) return hipSuccess;
-  const int K = (int)((n_tok + BW_CHUNK - 1) / BW_CHUNK);
+ScanBwdLayout scan_backward_layout(float* ws, int64_t n_tok, int d_inner) {
+  ScanBwdLayout w;
+  w.K = (int)((n_tok + BW_CHUNK - 1) / BW_CHUNK);
+  w.chunk = BW_CHUNK;
   const int64_t dn = (int64_t)d_inner * NS;
-  const int ncb = d_inner / BW_CH;
-  float* aggP = ws;
-  float* aggh = aggP + (int64_t)K * dn;
-  float* carry = aggh + (int64_t)K * dn;
-  float* Lb = carry + (int64_t)K * dn;
-  float* Iin = Lb + (int64_t)K * dn;
-  float* dA_part = Iin + (int64_t)K * dn;
-  float* dD_part = dA_part + (int64_t)K * dn;
-  float* bc_part = dD_part + (int64_t)K * d_inner;
-  hipError_t err;
-  if (K > 1) {
-    // 1. forward chunk-entry states at this chunk length
-    err = launch_scan_chunk_state<T>(x, dt, A_log, Bm, h0, nullptr, cu, aggP, aggh, n_seqs, n_tok,
-                                     d_inner, BW_CHUNK, K - 1, s);
-    if (err != hipSuccess) return err;
-    err = launch_scan_chunk_carry(aggP, aggh, carry, d_inner, K, s);
-    if (err != hipSuccess) return err;
-    // 2. adjoint each chunk sends back; 3. adjoint entering each chunk
-    hipLaunchKernelGGL(bwd_adjoint_kernel<T>, dim3(ncb, K - 1), dim3(256), 0, s, dg, z, dt,
-                       A_log, Cm, dh_last, cu, Lb, n_seqs, n_tok, d_inner);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s, Lb,
-                       aggP, Iin, dn, K);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  // 4. main
-  hipLaunchKernelGGL(bwd_main_kernel<T>, dim3(ncb, K), dim3(256), 0, s, x, dt, A_log, Bm, Cm, D,
-                     z, dg, h0, dh_last, carry, Iin, cu, dx, ddt, dz, bc_part, dA_part, dD_part,
-                     dh0, n_seqs, n_tok, d_inner);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  // 5. reductions
-  const int64_t nbc = n_tok * 2 * NS;
-  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s,
-                     bc_part, dB, dC, ncb, n_tok);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s,
-                     dA_part, dD_part, A_log, dA_log, dD, K, d_inner);
+  w.aggP = ws;
+  w.aggh = w.aggP + (int64_t)w.K * dn;
+  w.carry = w.aggh + (int64_t)w.K * dn;
+  w.L = w.carry + (int64_t)w.K * dn;
+  w.Iin = w.L + (int64_t)w.K * dn;
+  w.dA_part = w.Iin + (int64_t)w.K * dn;
+  w.dD_part = w.dA_part + (int64_t)w.K * dn;
+  w.bc_part = w.dD_part + (int64_t)w.K * d_inner;
+  return w;
+}
+
+template <typename T>
+hipError_t launch_scan_bwd_adjoint(const T* dg, const T* z, const float* dt, const float* A_log,
+                                   const float* Cm, const float* dh_last, const int32_t* cu,
+                                   const ScanBwdLayout& w, int n_seqs, int64_t n_tok, int d_inner,
+                                   hipStream_t s) {
+  if (w.K <= 1) return hipSuccess;
+  hipLaunchKernelGGL(bwd_adjoint_kernel<T>, dim3(d_inner / BW_CH, w.K - 1), dim3(256), 0, s, dg,
+                     z, dt, A_log, Cm, dh_last, cu, w.L, n_seqs, n_tok, d_inner);
   return hipGetLastError();
 }
 
-template hipError_t launch_scan_backward<float>(const float*, const float*, const float*,
-                                                const float*, const float*, const float*,
-                                                const float*, const float*, const float*,
-                                                const float*, const int32_t*, int, int64_t, int,
-                                                float*, float*, float*, float*, float*, float*,
-                                                float*, float*, float*, hipStream_t);
-template hipError_t launch_scan_backward<bf16>(const bf16*, const float*, const float*,
-                                               const float*, const float*, const float*,
-                                               const bf16*, const bf16*, const float*,
-                                               const float*, const int32_t*, int, int64_t, int,
-                                               float*, float*, float*, float*, float*, float*,
-                                               float*, float*, float*, hipStream_t);
+hipError_t launch_scan_bwd_carry(const ScanBwdLayout& w, int d_inner, hipStream_t s) {
+  if (w.K <= 1) return hipSuccess;
+  const int64_t dn = (int64_t)d_inner * NS;
+  hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s, w.L,
+                     w.aggP, w.Iin, dn, w.K);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scan_bwd_main(const T* x, const float* dt, const float* A_log, const float* Bm,
+                                const float* Cm, const float* D, const T* z, const T* dg,
+                                const float* h0, const float* dh_last, const int32_t* cu,
+                                const ScanBwdLayout& w, int n_seqs, int64_t n_tok, int d_inner,
+                                float* dx, float* ddt, float* dz, float* dh0, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_main_kernel<T>, dim3(d_inner / BW_CH, w.K), dim3(256), 0, s, x, dt, A_log,
+                     Bm, Cm, D, z, dg, h0, dh_last, w.carry, w.Iin, cu, dx, ddt, dz, w.bc_part,
+                     w.dA_part, w.dD_part, dh0, n_seqs, n_tok, d_inner);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_bwd_reduce(const ScanBwdLayout& w, const float* A_log, int64_t n_tok,
+                                  int d_inner, float* dB, float* dC, float* dA_log, float* dD,
+                                  hipStream_t s) {
+  const int64_t nbc = n_tok * 2 * NS;
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s,
+                     w.bc_part, dB, dC, d_inner / BW_CH, n_tok);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t dn = (int64_t)d_inner * NS;
+  hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s,
+                     w.dA_part, w.dD_part, A_log, dA_log, dD, w.K, d_inner);
+  return hipGetLastError();
+}
+
+#define JM_BWD_INST(T)                                                                          \
+  template hipError_t launch_scan_bwd_adjoint<T>(const T*, const T*, const float*, const float*, \
+                                                 const float*, const float*, const int32_t*,    \
+                                                 const ScanBwdLayout&, int, int64_t, int,        \
+                                                 hipStream_t);                                   \
+  template hipError_t launch_scan_bwd_main<T>(const T*, const float*, const float*, const float*,\
+                                              const float*, const float*, const T*, const T*,    \
+                                              const float*, const float*, const int32_t*,        \
+                                              const ScanBwdLayout&, int, int64_t, int, float*,   \
+                                              float*, float*, float*, hipStream_t);
+JM_BWD_INST(float)
+JM_BWD_INST(bf16)
 
 }  // namespace jm

@@ -21,15 +21,19 @@
 //   3. adjoint into each chunk (bwd_carry_kernel), sequential over chunks in reverse:
 //      I_{K-1} = 0, I_{k-1} = L_k + P_k I_k;
 //   4. main (bwd_main_kernel), per chunk: a forward pass from the entry state keeps the
-//      state before every 8-token sub-block in LDS; then, sub-block by sub-block from the
-//      end, the 8 states are recomputed into registers (with their decays) and the adjoint
-//      runs backwards from I_k, emitting per-token gradients;
+//      state before every 8-token sub-block (in registers, as a stack); then, sub-block by
+//      sub-block from the end, the 8 states after each token are recomputed into registers
+//      (with their decays) and the adjoint runs backwards from I_k, emitting per-token
+//      gradients;
 //   5. fixed-order reductions: dB and dC over channel blocks, dA_log and dD over chunks.
 // Lanes: thread = (channel d, quad q), q owning states 4q..4q+3; a workgroup of 256
-// threads covers 64 channels. Reductions over n run over the 4 lanes of a channel (lane
-// shuffles); dB and dC reduce over the wave's 16 channels by shuffles and over the
-// workgroup's 4 waves through LDS, then across workgroups in the fixed-order reduction.
-// All gradients are fp32. Deterministic: no atomics.
+// threads covers 64 channels. The chunk's Delta and x (and B, C) are copied once into LDS
+// with coalesced loads; dy and dz's factor dg SiLU'(z) are formed once per element when a
+// sub-block's z and dg are copied in, so the per-token work reads LDS only. Reductions over n
+// run over the 4 lanes of a channel (DPP quad permutes); dB and dC reduce over the 4 channels
+// of a 16-lane row by DPP row rotations, then over the workgroup's 16 rows in LDS, then
+// across workgroups in the fixed-order reduction. Per-token outputs go through LDS and leave
+// as whole rows. All gradients are fp32. Deterministic: no atomics.
 #include "jm_internal.h"
 
 namespace jm {
@@ -54,23 +58,6 @@ __device__ __forceinline__ float sigm(float v) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp(-v));
 }
 
-// Lane layout helpers.
-struct Lane {
-  int d;      // channel
-  int q;      // quad: states 4q..4q+3
-  int lane;   // lane in the wave
-  int wave;
-};
-
-__device__ __forceinline__ Lane lane_of(int cblock) {
-  Lane L;
-  L.lane = threadIdx.x & 63;
-  L.wave = threadIdx.x >> 6;
-  L.q = threadIdx.x & 3;
-  L.d = cblock * BW_CH + (threadIdx.x >> 2);
-  return L;
-}
-
 __device__ __forceinline__ void load4(const float* p, float v[4]) {
   const float4 f = *reinterpret_cast<const float4*>(p);
   v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
@@ -78,26 +65,71 @@ __device__ __forceinline__ void load4(const float* p, float v[4]) {
 __device__ __forceinline__ void store4(float* p, const float v[4]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ void zero4(float v[4]) { v[0] = v[1] = v[2] = v[3] = 0.0f; }
 
-// Sum over the 4 lanes of a channel.
+// 4 / 2 consecutive activations as fp32 (bf16: the bit pattern shifted into the high half).
+__device__ __forceinline__ void load4f(const float* p, float v[4]) { load4(p, v); }
+__device__ __forceinline__ void load4f(const bf16* p, float v[4]) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
+  v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+__device__ __forceinline__ void load2f(const float* p, float v[2]) {
+  const float2 f = *reinterpret_cast<const float2*>(p);
+  v[0] = f.x; v[1] = f.y;
+}
+__device__ __forceinline__ void load2f(const bf16* p, float v[2]) {
+  const uint32_t r = *reinterpret_cast<const uint32_t*>(p);
+  v[0] = __uint_as_float(r << 16); v[1] = __uint_as_float(r & 0xffff0000u);
+}
+
+// Lane exchange through DPP (the add folds into v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, true));
+}
+// Sum over the 4 lanes of a channel (quad permutes [1,0,3,2] then [2,3,0,1]).
 __device__ __forceinline__ float quad_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
+#pragma clang fp contract(off)   // keep the adds separate so they fold into v_add_f32_dpp
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
   return v;
 }
-// Sum over the 16 channels of a wave for one quad position (lanes q, q+4, ..., q+60).
-__device__ __forceinline__ float wave_channel_sum(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
+// Sum over the 4 channels of a 16-lane row, per quad position (row rotations by 4 and 8).
+__device__ __forceinline__ float row_channel_sum(float v) {
+#pragma clang fp contract(off)
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
   return v;
 }
 
+// dy = dg SiLU(z) and gz = dg SiLU'(z), SiLU'(z) = s (1 + z (1 - s)), s = sigmoid(z).
+__device__ __forceinline__ float2 dy_gz(float zv, float gv) {
+  const float sg = sigm(zv);
+  return make_float2(gv * zv * sg, gv * sg * fmaf(zv, 1.0f - sg, 1.0f));
+}
+
+// Copies rows [0, nrows) of a chunk's (Delta, x) into LDS as {Delta, x} pairs: thread =
+// (row tid/16 + 16 j, channels 4 (tid % 16) .. +3); rows past nrows are zero.
 template <typename T>
-__device__ __forceinline__ float dy_of(const T* dg, const T* z, int64_t o) {
-  const float zv = to_f32(z[o]);
-  return to_f32(dg[o]) * zv * sigm(zv);
+__device__ __forceinline__ void stage_dtx(float2 (*sxd)[BW_CH], const float* __restrict__ dt,
+                                          const T* __restrict__ x, int64_t s, int nrows,
+                                          int c0, int d_inner) {
+  const int cc = 4 * (threadIdx.x & 15);
+#pragma unroll
+  for (int j = 0; j < BW_CHUNK / 16; ++j) {
+    const int r = (threadIdx.x >> 4) + 16 * j;
+    float dv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r < nrows) {
+      const int64_t o = (s + r) * d_inner + c0 + cc;
+      load4(dt + o, dv);
+      load4f(x + o, xv);
+    }
+    float4* dst = reinterpret_cast<float4*>(&sxd[r][cc]);
+    dst[0] = make_float4(dv[0], xv[0], dv[1], xv[1]);
+    dst[1] = make_float4(dv[2], xv[2], dv[3], xv[3]);
+  }
 }
 
 // ---- 2. adjoint sent by chunk k (k >= 1) to chunk k-1 ------------------------------------
@@ -108,33 +140,56 @@ void bwd_adjoint_kernel(const T* __restrict__ dg, const T* __restrict__ z,
                         const float* __restrict__ Cm, const float* __restrict__ dh_last,
                         const int32_t* __restrict__ cu, float* __restrict__ Lout, int n_seqs,
                         int64_t n_tok, int d_inner) {
-  const Lane L = lane_of(blockIdx.x);
+  __shared__ float2 sdy[BW_CHUNK][BW_CH];         // {Delta, dy}
+  __shared__ float4 sc[BW_CHUNK][4];              // C_t[4q..4q+3]
+  const int q = threadIdx.x & 3;
+  const int c0 = blockIdx.x * BW_CH;
+  const int d = c0 + (threadIdx.x >> 2);
   const int k = blockIdx.y + 1;
   const int64_t s = (int64_t)k * BW_CHUNK;
   const int64_t e = s + BW_CHUNK < n_tok ? s + BW_CHUNK : n_tok;
+  const int64_t dn4 = (int64_t)d * NS + 4 * q;
   float lam[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const int i = find_seq_b(cu, n_seqs, s);
-  float* out = Lout + ((int64_t)k * d_inner + L.d) * NS + 4 * L.q;
+  float* out = Lout + (int64_t)k * d_inner * NS + dn4;
   if (cu[i] == s) {                      // nothing flows into another sequence
     store4(out, lam);
     return;
   }
   const int64_t e1 = cu[i + 1] < e ? cu[i + 1] : e;
-  if (e1 == cu[i + 1] && dh_last) load4(dh_last + ((int64_t)i * d_inner + L.d) * NS + 4 * L.q, lam);
+  const int n1 = (int)(e1 - s);          // tokens of the chunk's first sequence segment
+  {
+    const int cc = 4 * (threadIdx.x & 15);
+#pragma unroll
+    for (int j = 0; j < BW_CHUNK / 16; ++j) {
+      const int r = (threadIdx.x >> 4) + 16 * j;
+      if (r < n1) {
+        const int64_t o = (s + r) * d_inner + c0 + cc;
+        float dv[4], zv[4], gv[4];
+        load4(dt + o, dv);
+        load4f(z + o, zv);
+        load4f(dg + o, gv);
+        float4* dst = reinterpret_cast<float4*>(&sdy[r][cc]);
+        dst[0] = make_float4(dv[0], dy_gz(zv[0], gv[0]).x, dv[1], dy_gz(zv[1], gv[1]).x);
+        dst[1] = make_float4(dv[2], dy_gz(zv[2], gv[2]).x, dv[3], dy_gz(zv[3], gv[3]).x);
+      }
+    }
+    const int r = threadIdx.x >> 2;
+    if (r < n1) sc[r][q] = *reinterpret_cast<const float4*>(Cm + (s + r) * NS + 4 * q);
+  }
+  if (e1 == cu[i + 1] && dh_last) load4(dh_last + (int64_t)i * d_inner * NS + dn4, lam);
   float a2[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a2[j] = -fast_exp(A_log[(int64_t)L.d * NS + 4 * L.q + j]) * kLog2e;
-  for (int64_t t = e1 - 1; t >= s; --t) {
-    const int64_t o = t * d_inner + L.d;
-    const float dy = dy_of(dg, z, o);
-    const float dtv = dt[o];
-    float c[4];
-    load4(Cm + t * NS + 4 * L.q, c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lam[j] = fmaf(dy, c[j], lam[j]);
-      lam[j] *= __builtin_amdgcn_exp2f(dtv * a2[j]);     // flows to t-1
-    }
+  for (int j = 0; j < 4; ++j) a2[j] = -fast_exp(A_log[dn4 + j]) * kLog2e;
+  __syncthreads();
+  const int dl = threadIdx.x >> 2;
+  for (int r = n1 - 1; r >= 0; --r) {
+    const float2 v = sdy[r][dl];
+    const float4 c = sc[r][q];
+    lam[0] = fmaf(v.y, c.x, lam[0]) * __builtin_amdgcn_exp2f(v.x * a2[0]);   // flows to t-1
+    lam[1] = fmaf(v.y, c.y, lam[1]) * __builtin_amdgcn_exp2f(v.x * a2[1]);
+    lam[2] = fmaf(v.y, c.z, lam[2]) * __builtin_amdgcn_exp2f(v.x * a2[2]);
+    lam[3] = fmaf(v.y, c.w, lam[3]) * __builtin_amdgcn_exp2f(v.x * a2[3]);
   }
   store4(out, lam);
 }
@@ -156,7 +211,21 @@ void bwd_carry_kernel(const float* __restrict__ Lin, const float* __restrict__ P
   }
 }
 
-// ---- 4. main: per chunk, states recomputed from LDS checkpoints, adjoint backwards ----------
+// ---- 4. main: per chunk, states recomputed from checkpoints, adjoint backwards --------------
+// z and dg of one sub-block, for the {dy, gz} copy: thread = (token tid/32, channels
+// 2 (tid % 32), +1).
+template <typename T>
+__device__ __forceinline__ void fetch_zg(const T* __restrict__ z, const T* __restrict__ dg,
+                                         int64_t t, int64_t e, int64_t col, int d_inner,
+                                         float zr[2], float gr[2]) {
+  if (t < e) {
+    load2f(z + t * d_inner + col, zr);
+    load2f(dg + t * d_inner + col, gr);
+  } else {
+    zr[0] = zr[1] = gr[0] = gr[1] = 0.0f;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256)
 void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
@@ -170,83 +239,137 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                      float* __restrict__ dBC_part, float* __restrict__ dA_part,
                      float* __restrict__ dD_part, float* __restrict__ dh0, int n_seqs,
                      int64_t n_tok, int d_inner) {
-  __shared__ float4 ck[NSUB][256];                 // state before each sub-block, per lane
-  __shared__ float stage[SUB][4][2 * NS];          // per-wave dB | dC of each sub-block token
-  const Lane L = lane_of(blockIdx.x);
+  __shared__ float2 sxd[BW_CHUNK][BW_CH];   // {Delta, x}; {dDelta, dz} once a token is done
+  __shared__ float2 sgy[2][SUB][BW_CH];     // {dy, gz} of a sub-block (two buffers); dx once done
+  __shared__ float4 sbc[BW_CHUNK][8];       // [t][q] = B_t[4q..4q+3], [t][4 + q] = C_t[4q..4q+3]
+  __shared__ float red[SUB][16][2 * NS];    // per-row partials of dB | dC, per token
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = tid & 3;
+  const int dl = tid >> 2;                  // channel within the workgroup
+  const int c0 = blockIdx.x * BW_CH;
+  const int d = c0 + dl;
   const int k = blockIdx.y;
   const int64_t s = (int64_t)k * BW_CHUNK;
   const int64_t e = s + BW_CHUNK < n_tok ? s + BW_CHUNK : n_tok;
-  const int64_t dn4 = (int64_t)L.d * NS + 4 * L.q;   // this lane's 4 states in a (d, n) row
+  const int nt = (int)(e - s);
+  const int nsub = (nt + SUB - 1) / SUB;
+  const int64_t dn = (int64_t)d_inner * NS;
+  const int64_t dn4 = (int64_t)d * NS + 4 * q;   // this lane's 4 states in a (d, n) row
+  const int su = tid >> 5;                       // copy / write-out map: token of a sub-block
+  const int scp = 2 * (tid & 31);                //   and channel pair
+
+  // the chunk's {Delta, x}, B and C; {dy, gz} of the last sub-block
+  stage_dtx<T>(sxd, dt, x, s, nt, c0, d_inner);
+  if (dl < nt) {
+    sbc[dl][q] = *reinterpret_cast<const float4*>(Bm + (s + dl) * NS + 4 * q);
+    sbc[dl][4 + q] = *reinterpret_cast<const float4*>(Cm + (s + dl) * NS + 4 * q);
+  }
+  float zr[2], gr[2];
+  fetch_zg(z, dg, s + (int64_t)(nsub - 1) * SUB + su, e, c0 + scp, d_inner, zr, gr);
+  {
+    const float2 a = dy_gz(zr[0], gr[0]), b = dy_gz(zr[1], gr[1]);
+    *reinterpret_cast<float4*>(&sgy[(nsub - 1) & 1][su][scp]) = make_float4(a.x, a.y, b.x, b.y);
+  }
   float A4[4], a2[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     A4[j] = -fast_exp(A_log[dn4 + j]);
     a2[j] = A4[j] * kLog2e;
   }
-  const float Dd = Dv[L.d];
+  const float Dd = Dv[d];
+  __syncthreads();
 
-  // pass 1: forward from the entry state, keeping the state before each sub-block
-  int i = find_seq_b(cu, n_seqs, s);
-  float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (cu[i] != s) {
-    load4(carry + (int64_t)k * d_inner * NS + dn4, h);   // k >= 1 here
-  }
-  for (int64_t t = s; t < e; ++t) {
-    if (t == cu[i + 1]) ++i;
-    if (t == cu[i]) {                                     // sequence start: initial state
-      if (h0) load4(h0 + (int64_t)i * d_inner * NS + dn4, h);
-      else h[0] = h[1] = h[2] = h[3] = 0.0f;
+  // pass 1: forward from the entry state; the state entering each sub-block is pushed on a
+  // register stack (ck[NSUB - 1] is the top)
+  float ck[NSUB][4];
+  {
+    int i = find_seq_b(cu, n_seqs, s);
+    float h[4];
+    if (cu[i] == s) {
+      if (h0) load4(h0 + (int64_t)i * dn + dn4, h); else zero4(h);
+    } else {
+      load4(carry + (int64_t)k * dn + dn4, h);     // k >= 1 here
     }
-    if (((t - s) & (SUB - 1)) == 0) ck[(t - s) / SUB][threadIdx.x] = make_float4(h[0], h[1], h[2], h[3]);
-    const int64_t o = t * d_inner + L.d;
-    const float dtv = dt[o];
-    const float dxv = dtv * to_f32(x[o]);
-    float b[4];
-    load4(Bm + t * NS + 4 * L.q, b);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) h[j] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[j]), h[j], dxv * b[j]);
-  }
-
-  // pass 2: backwards. lam = adjoint arriving at the current token from later ones.
-  int ie = find_seq_b(cu, n_seqs, e - 1);
-  float lam[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (cu[ie + 1] == e) {
-    if (dh_last) load4(dh_last + (int64_t)ie * d_inner * NS + dn4, lam);
-  } else {
-    load4(Iin + (int64_t)k * d_inner * NS + dn4, lam);
-  }
-  float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float dDacc = 0.0f;
-  const int nsub = (int)((e - s + SUB - 1) / SUB);
-  int iseq = ie;                                          // sequence of the current token
-  for (int sb = nsub - 1; sb >= 0; --sb) {
-    const int64_t t0 = s + (int64_t)sb * SUB;
-    const int len = (int)(e - t0 < SUB ? e - t0 : SUB);
-    // recompute the sub-block's states before each token, and its decays
-    float hp[SUB][4], av[SUB][4];
-    {
-      const float4 c4 = ck[sb][threadIdx.x];
-      float hh[4] = {c4.x, c4.y, c4.z, c4.w};
-      int ii = find_seq_b(cu, n_seqs, t0);
+    int nstart = cu[i + 1];                        // next sequence start (n_tok if none)
+    for (int sb = 0; sb < nsub; ++sb) {
+      const int r0 = sb * SUB;
+      const int len = nt - r0 < SUB ? nt - r0 : SUB;
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
         if (u < len) {
-          const int64_t t = t0 + u;
-          if (u > 0 && t == cu[ii + 1]) {                 // a sequence starts inside
-            ++ii;
-            if (h0) load4(h0 + (int64_t)ii * d_inner * NS + dn4, hh);
-            else hh[0] = hh[1] = hh[2] = hh[3] = 0.0f;
+          if (s + r0 + u == nstart) {                // a sequence starts: its initial state
+            ++i;
+            nstart = cu[i + 1];
+            if (h0) load4(h0 + (int64_t)i * dn + dn4, h); else zero4(h);
           }
-          const int64_t o = t * d_inner + L.d;
-          const float dtv = dt[o];
-          const float dxv = dtv * to_f32(x[o]);
-          float b[4];
-          load4(Bm + t * NS + 4 * L.q, b);
+          if (u == 0) {
+#pragma unroll
+            for (int m = 0; m < NSUB - 1; ++m)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) ck[m][j] = ck[m + 1][j];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ck[NSUB - 1][j] = h[j];
+          }
+          const float2 v = sxd[r0 + u][dl];
+          const float4 b = sbc[r0 + u][q];
+          const float dtx = v.x * v.y;
+          h[0] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[0]), h[0], dtx * b.x);
+          h[1] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[1]), h[1], dtx * b.y);
+          h[2] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[2]), h[2], dtx * b.z);
+          h[3] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[3]), h[3], dtx * b.w);
+        }
+      }
+    }
+  }
+
+  // pass 2: backwards. lam = adjoint arriving at the current token from later ones.
+  int iseq = find_seq_b(cu, n_seqs, e - 1);               // sequence of the current token
+  float lam[4];
+  if (cu[iseq + 1] == e) {
+    if (dh_last) load4(dh_last + (int64_t)iseq * dn + dn4, lam); else zero4(lam);
+  } else {
+    load4(Iin + (int64_t)k * dn + dn4, lam);
+  }
+  float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dDacc = 0.0f;
+  for (int sb = nsub - 1; sb >= 0; --sb) {
+    const int p = sb & 1;
+    const int r0 = sb * SUB;
+    const int64_t t0 = s + r0;
+    const int len = nt - r0 < SUB ? nt - r0 : SUB;
+    if (sb > 0) fetch_zg(z, dg, t0 - SUB + su, e, c0 + scp, d_inner, zr, gr);
+    // hq[u + 1] = state after token u, hq[0] = state entering the sub-block; av = decays
+    float hq[SUB + 1][4], av[SUB][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hq[0][j] = ck[NSUB - 1][j];
+#pragma unroll
+    for (int m = NSUB - 1; m > 0; --m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ck[m][j] = ck[m - 1][j];
+    {
+      int ii = iseq;
+      while (cu[ii] > t0) --ii;
+      int ns = cu[ii + 1];
+      float hh[4] = {hq[0][0], hq[0][1], hq[0][2], hq[0][3]};
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        if (u < len) {
+          if (u > 0 && t0 + u == ns) {               // a sequence starts inside
+            ++ii;
+            ns = cu[ii + 1];
+            if (h0) load4(h0 + (int64_t)ii * dn + dn4, hh); else zero4(hh);
+          }
+          const float2 v = sxd[r0 + u][dl];
+          const float4 b = sbc[r0 + u][q];
+          const float dtx = v.x * v.y;
+          const float bb[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            hp[u][j] = hh[j];
-            av[u][j] = __builtin_amdgcn_exp2f(dtv * a2[j]);
-            hh[j] = fmaf(av[u][j], hh[j], dxv * b[j]);
+            av[u][j] = __builtin_amdgcn_exp2f(v.x * a2[j]);
+            hh[j] = fmaf(av[u][j], hh[j], dtx * bb[j]);
+            hq[u + 1][j] = hh[j];
           }
         }
       }
@@ -259,74 +382,86 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
         // t ends its sequence inside the chunk: nothing arrives from the next sequence
         // (the chunk's last token got its incoming adjoint before the loop)
         if (t + 1 == cu[iseq + 1] && t + 1 < e) {
-          if (dh_last) load4(dh_last + (int64_t)iseq * d_inner * NS + dn4, lam);
-          else lam[0] = lam[1] = lam[2] = lam[3] = 0.0f;
+          if (dh_last) load4(dh_last + (int64_t)iseq * dn + dn4, lam); else zero4(lam);
         }
-        const int64_t o = t * d_inner + L.d;
-        const float dtv = dt[o];
-        const float xv = to_f32(x[o]);
-        const float zv = to_f32(z[o]);
-        const float gv = to_f32(dg[o]);
-        const float sg = sigm(zv);
-        const float dy = gv * zv * sg;
-        float b[4], c[4];
-        load4(Bm + t * NS + 4 * L.q, b);
-        load4(Cm + t * NS + 4 * L.q, c);
-        float ypart = 0.0f, ddt_part = 0.0f, dx_part = 0.0f;
+        const bool start = t == cu[iseq];
+        float hp[4];
+        if (start && u > 0) {                             // state before t: the initial one
+          if (h0) load4(h0 + (int64_t)iseq * dn + dn4, hp); else zero4(hp);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) hp[j] = hq[u][j];
+        }
+        const float2 v = sxd[r0 + u][dl];
+        const float2 gy = sgy[p][u][dl];
+        const float4 b4 = sbc[r0 + u][q];
+        const float4 c4 = sbc[r0 + u][4 + q];
+        const float dtv = v.x, xv = v.y, dy = gy.x, gz = gy.y;
+        const float dtx = dtv * xv;
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w};
+        float yp = 0.0f, ddtA = 0.0f, dxp = 0.0f;
         float dBv[4], dCv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float ht = fmaf(av[u][j], hp[u][j], dtv * xv * b[j]);
-          ypart = fmaf(c[j], ht, ypart);
+          const float ht = hq[u + 1][j];
+          yp = fmaf(cc[j], ht, yp);
           dCv[j] = dy * ht;
-          const float lt = fmaf(dy, c[j], lam[j]);                 // lam_t
-          const float da = lt * hp[u][j];
-          const float dda = da * av[u][j];
-          ddt_part = fmaf(dda, A4[j], fmaf(lt * b[j], xv, ddt_part));
+          const float lt = fmaf(dy, cc[j], lam[j]);              // lam_t
+          const float dda = lt * hp[j] * av[u][j];               // dL/d(a_t) a_t
+          ddtA = fmaf(dda, A4[j], ddtA);
           dA[j] = fmaf(dda, dtv, dA[j]);
-          dBv[j] = lt * dtv * xv;
-          dx_part = fmaf(lt, b[j], dx_part);
-          lam[j] = av[u][j] * lt;                                  // flows to t-1
+          dxp = fmaf(lt, bb[j], dxp);
+          dBv[j] = lt * dtx;
+          lam[j] = av[u][j] * lt;                                // flows to t-1
         }
-        ypart = quad_sum(ypart);
-        ddt_part = quad_sum(ddt_part);
-        dx_part = quad_sum(dx_part);
-        if (L.q == 0) {
-          const float y = fmaf(Dd, xv, ypart);
-          dx[o] = fmaf(dx_part, dtv, dy * Dd);
-          ddt[o] = ddt_part;
-          dz[o] = gv * y * sg * (1.0f + zv * (1.0f - sg));
+        yp = quad_sum(yp);
+        ddtA = quad_sum(ddtA);
+        dxp = quad_sum(dxp);
+        if (q == 0) {
+          const float y = fmaf(Dd, xv, yp);
+          sxd[r0 + u][dl] = make_float2(fmaf(xv, dxp, ddtA), gz * y);   // dDelta, dz
+          sgy[p][u][dl].x = fmaf(dxp, dtv, dy * Dd);                     // dx
           dDacc = fmaf(dy, xv, dDacc);
         }
-        if (t == cu[iseq] && dh0) store4(dh0 + (int64_t)iseq * d_inner * NS + dn4, lam);
-        // dB, dC: sum over the wave's 16 channels, then stage per wave
+        if (start && dh0) store4(dh0 + (int64_t)iseq * dn + dn4, lam);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          dBv[j] = wave_channel_sum(dBv[j]);
-          dCv[j] = wave_channel_sum(dCv[j]);
+          dBv[j] = row_channel_sum(dBv[j]);
+          dCv[j] = row_channel_sum(dCv[j]);
         }
-        if (L.lane < 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            stage[u][L.wave][4 * L.q + j] = dBv[j];
-            stage[u][L.wave][NS + 4 * L.q + j] = dCv[j];
-          }
+        if ((lane & 12) == 0) {                        // channel 0 of each row: the row's sums
+          const int pr = tid >> 4;                     // row within the workgroup
+          *reinterpret_cast<float4*>(&red[u][pr][4 * q]) = make_float4(dBv[0], dBv[1], dBv[2], dBv[3]);
+          *reinterpret_cast<float4*>(&red[u][pr][NS + 4 * q]) =
+              make_float4(dCv[0], dCv[1], dCv[2], dCv[3]);
         }
       }
     }
     __syncthreads();
-    // workgroup partial of dB | dC for the sub-block's tokens: thread = (token, value)
-    {
-      const int u = threadIdx.x >> 5, v = threadIdx.x & 31;
-      if (u < len) {
-        const float sum = (stage[u][0][v] + stage[u][1][v]) + (stage[u][2][v] + stage[u][3][v]);
-        dBC_part[((int64_t)blockIdx.x * n_tok + t0 + u) * (2 * NS) + v] = sum;
-      }
+    // write-out: dB | dC partial of the workgroup (thread = token su, value tid % 32) and the
+    // sub-block's dx, dDelta, dz rows (thread = token su, channels scp, scp + 1)
+    if (su < len) {
+      const int64_t t = t0 + su;
+      const int v = tid & 31;
+      float sum = 0.0f;
+#pragma unroll
+      for (int pr = 0; pr < 16; ++pr) sum += red[su][pr][v];
+      dBC_part[((int64_t)blockIdx.x * n_tok + t) * (2 * NS) + v] = sum;
+      const float4 o1 = *reinterpret_cast<const float4*>(&sxd[r0 + su][scp]);
+      const float4 o2 = *reinterpret_cast<const float4*>(&sgy[p][su][scp]);
+      const int64_t o = t * d_inner + c0 + scp;
+      *reinterpret_cast<float2*>(ddt + o) = make_float2(o1.x, o1.z);
+      *reinterpret_cast<float2*>(dz + o) = make_float2(o1.y, o1.w);
+      *reinterpret_cast<float2*>(dx + o) = make_float2(o2.x, o2.z);
+    }
+    if (sb > 0) {                                      // {dy, gz} of the next sub-block
+      const float2 a = dy_gz(zr[0], gr[0]), b = dy_gz(zr[1], gr[1]);
+      *reinterpret_cast<float4*>(&sgy[p ^ 1][su][scp]) = make_float4(a.x, a.y, b.x, b.y);
     }
     __syncthreads();
   }
-  store4(dA_part + (int64_t)k * d_inner * NS + dn4, dA);
-  if (L.q == 0) dD_part[(int64_t)k * d_inner + L.d] = dDacc;
+  store4(dA_part + (int64_t)k * dn + dn4, dA);
+  if (q == 0) dD_part[(int64_t)k * d_inner + d] = dDacc;
 }
 
 // ---- 5. fixed-order reductions ---------------------------------------------------------

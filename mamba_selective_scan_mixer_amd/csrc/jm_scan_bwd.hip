@@ -67,6 +67,59 @@ __device__ __forceinline__ void store4(float* p, const float v[4]) {
 }
 __device__ __forceinline__ void zero4(float v[4]) { v[0] = v[1] = v[2] = v[3] = 0.0f; }
 
+// Buffer-resource accesses: a wave-uniform base (scalar registers) plus a 32-bit per-lane
+// byte offset. The main loop's addresses then never become 64-bit per-lane pointers, which the
+// compiler would otherwise hoist out of the loop and keep live (or spill) for every array.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+#endif
+__device__ __forceinline__ uint32_t ld_b32(const void* base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b32(rsrc_at(base), (int)off, 0, 0);
+#else
+  return 0u;
+#endif
+}
+__device__ __forceinline__ uint2 ld_b64(const void* base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rsrc_at(base), (int)off, 0, 0);
+  return make_uint2(v[0], v[1]);
+#else
+  return make_uint2(0u, 0u);
+#endif
+}
+// A lane's 4 states of a (d_inner, 16) state row (`lo` = its byte offset in the row).
+__device__ __forceinline__ void ld4_at(const float* row, uint32_t lo, float v[4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rsrc_at(row), (int)lo, 0, 0);
+  v[0] = __uint_as_float(r[0]); v[1] = __uint_as_float(r[1]);
+  v[2] = __uint_as_float(r[2]); v[3] = __uint_as_float(r[3]);
+#endif
+}
+__device__ __forceinline__ void st4_at(float* row, uint32_t lo, const float v[4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const u32x4 r = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                   __float_as_uint(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(r, rsrc_at(row), (int)lo, 0, 0);
+#endif
+}
+__device__ __forceinline__ void st2_at(float* row, uint32_t lo, float a, float b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const u32x2 r = {__float_as_uint(a), __float_as_uint(b)};
+  __builtin_amdgcn_raw_buffer_store_b64(r, rsrc_at(row), (int)lo, 0, 0);
+#endif
+}
+__device__ __forceinline__ void st1_at(float* row, uint32_t lo, float a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), rsrc_at(row), (int)lo, 0, 0);
+#endif
+}
+
 // 4 / 2 consecutive activations as fp32 (bf16: the bit pattern shifted into the high half).
 __device__ __forceinline__ void load4f(const float* p, float v[4]) { load4(p, v); }
 __device__ __forceinline__ void load4f(const bf16* p, float v[4]) {
@@ -212,22 +265,208 @@ void bwd_carry_kernel(const float* __restrict__ Lin, const float* __restrict__ P
 }
 
 // ---- 4. main: per chunk, states recomputed from checkpoints, adjoint backwards --------------
-// z and dg of one sub-block, for the {dy, gz} copy: thread = (token tid/32, channels
-// 2 (tid % 32), +1).
+// z and dg of one sub-block for the {dy, gz} copy, kept as raw bits until they are used
+// (so the loads stay in flight across the sub-block's work): thread = (token tid/32,
+// channels 2 (tid % 32), +1).
+struct RawZg {
+  uint2 z, g;
+};
+__device__ __forceinline__ void load_raw2(const float* row, uint32_t lo, uint2& r) {
+  r = ld_b64(row, lo);
+}
+__device__ __forceinline__ void load_raw2(const bf16* row, uint32_t lo, uint2& r) {
+  r.x = ld_b32(row, lo);
+  r.y = 0u;
+}
+template <typename T> __device__ __forceinline__ void unpack2(uint2 r, float v[2]);
+template <> __device__ __forceinline__ void unpack2<float>(uint2 r, float v[2]) {
+  v[0] = __uint_as_float(r.x); v[1] = __uint_as_float(r.y);
+}
+template <> __device__ __forceinline__ void unpack2<bf16>(uint2 r, float v[2]) {
+  v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
+}
+
+// Rows t0 .. t0 + SUB - 1 of z and dg: `lo` = this thread's byte offset from row t0 (token
+// tid/32, channels 2 (tid % 32), +1), `valid` = its token is before the chunk's end.
 template <typename T>
 __device__ __forceinline__ void fetch_zg(const T* __restrict__ z, const T* __restrict__ dg,
-                                         int64_t t, int64_t e, int64_t col, int d_inner,
-                                         float zr[2], float gr[2]) {
-  if (t < e) {
-    load2f(z + t * d_inner + col, zr);
-    load2f(dg + t * d_inner + col, gr);
+                                         int64_t t0, int d_inner, uint32_t lo, bool valid,
+                                         RawZg& r) {
+  if (valid) {
+    load_raw2(z + t0 * d_inner, lo, r.z);
+    load_raw2(dg + t0 * d_inner, lo, r.g);
   } else {
-    zr[0] = zr[1] = gr[0] = gr[1] = 0.0f;
+    r.z = r.g = make_uint2(0u, 0u);
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256)
+__device__ __forceinline__ void put_gy(float2 (*sgyb)[BW_CH], int su, int scp, const RawZg& r) {
+  float zv[2], gv[2];
+  unpack2<T>(r.z, zv);
+  unpack2<T>(r.g, gv);
+  const float2 a = dy_gz(zv[0], gv[0]), b = dy_gz(zv[1], gv[1]);
+  *reinterpret_cast<float4*>(&sgyb[su][scp]) = make_float4(a.x, a.y, b.x, b.y);
+}
+
+// Forward over one sub-block (pass 1). CHECK: the sub-block may be short or hold a sequence
+// start after its first token (then the state restarts there); without it, neither happens.
+template <bool CHECK>
+__device__ __forceinline__ void forward_sub(const float2 (*sxd)[BW_CH], const float4 (*sbc)[8],
+                                            int r0, int len, int64_t t0, int dl, int q,
+                                            const float (&a2)[4], float (&h)[4], int& i,
+                                            int& nstart, const int32_t* __restrict__ cu,
+                                            const float* __restrict__ h0, int64_t dn,
+                                            uint32_t lo4) {
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    if (!CHECK || u < len) {
+      if (CHECK && u > 0 && t0 + u == nstart) {
+        ++i;
+        nstart = cu[i + 1];
+        if (h0) ld4_at(h0 + (int64_t)i * dn, lo4, h); else zero4(h);
+      }
+      const float2 v = sxd[r0 + u][dl];
+      const float4 b = sbc[r0 + u][q];
+      const float dtx = v.x * v.y;
+      h[0] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[0]), h[0], dtx * b.x);
+      h[1] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[1]), h[1], dtx * b.y);
+      h[2] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[2]), h[2], dtx * b.z);
+      h[3] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[3]), h[3], dtx * b.w);
+    }
+  }
+}
+
+// The sub-block's states after each token (hq[u + 1]; hq[0] = state entering it) and decays.
+// ii = sequence of the sub-block's first token.
+template <bool CHECK>
+__device__ __forceinline__ void recompute_sub(const float2 (*sxd)[BW_CH],
+                                              const float4 (*sbc)[8], int r0, int len,
+                                              int64_t t0, int dl, int q, const float (&a2)[4],
+                                              float (&hq)[SUB + 1][4], float (&av)[SUB][4],
+                                              int ii, const int32_t* __restrict__ cu,
+                                              const float* __restrict__ h0, int64_t dn,
+                                              uint32_t lo4) {
+  int ns = CHECK ? cu[ii + 1] : 0;
+  float hh[4] = {hq[0][0], hq[0][1], hq[0][2], hq[0][3]};
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    if (!CHECK || u < len) {
+      if (CHECK && u > 0 && t0 + u == ns) {             // a sequence starts inside
+        ++ii;
+        ns = cu[ii + 1];
+        if (h0) ld4_at(h0 + (int64_t)ii * dn, lo4, hh); else zero4(hh);
+      }
+      const float2 v = sxd[r0 + u][dl];
+      const float4 b = sbc[r0 + u][q];
+      const float dtx = v.x * v.y;
+      const float bb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[u][j] = __builtin_amdgcn_exp2f(v.x * a2[j]);
+        hh[j] = fmaf(av[u][j], hh[j], dtx * bb[j]);
+        hq[u + 1][j] = hh[j];
+      }
+    }
+  }
+}
+
+// The adjoint backwards over one sub-block, with every per-token gradient. CHECK: the
+// sub-block may be short or hold sequence boundaries (the adjoint restarts where a sequence
+// ends, the state before a sequence's first token is its initial state, dL/dh0 is written
+// at a sequence's first token); without it the caller handles the sub-block's edges.
+template <bool CHECK>
+__device__ __forceinline__ void reverse_sub(float2 (*sxd)[BW_CH], float2 (*sgyb)[BW_CH],
+                                            const float4 (*sbc)[8], float (*red)[16][2 * NS],
+                                            int r0, int len, int64_t t0, int64_t e, int dl,
+                                            int q, int lane, int tid,
+                                            const float (&hq)[SUB + 1][4],
+                                            const float (&av)[SUB][4], const float (&A4)[4],
+                                            float Dd, float (&lam)[4], float (&dA)[4],
+                                            float& dDacc, int& iseq,
+                                            const int32_t* __restrict__ cu,
+                                            const float* __restrict__ h0,
+                                            const float* __restrict__ dh_last,
+                                            float* __restrict__ dh0, int64_t dn, uint32_t lo4) {
+#pragma unroll
+  for (int u = SUB - 1; u >= 0; --u) {
+    if (!CHECK || u < len) {
+      const int64_t t = t0 + u;
+      bool start = false;
+      if (CHECK) {
+        while (cu[iseq] > t) --iseq;                      // sequence of token t
+        // t ends its sequence inside the chunk: nothing arrives from the next sequence
+        // (the chunk's last token got its incoming adjoint before the loop)
+        if (t + 1 == cu[iseq + 1] && t + 1 < e) {
+          if (dh_last) ld4_at(dh_last + (int64_t)iseq * dn, lo4, lam); else zero4(lam);
+        }
+        start = t == cu[iseq];
+      }
+      float hp[4];
+      if (CHECK && start && u > 0) {                      // state before t: the initial one
+        if (h0) ld4_at(h0 + (int64_t)iseq * dn, lo4, hp); else zero4(hp);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hp[j] = hq[u][j];
+      }
+      const float2 v = sxd[r0 + u][dl];
+      const float2 gy = sgyb[u][dl];
+      const float4 b4 = sbc[r0 + u][q];
+      const float4 c4 = sbc[r0 + u][4 + q];
+      const float dtv = v.x, xv = v.y, dy = gy.x, gz = gy.y;
+      const float dtx = dtv * xv;
+      const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w};
+      float yp = 0.0f, ddtA = 0.0f, dxp = 0.0f;
+      float dBv[4], dCv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float ht = hq[u + 1][j];
+        yp = fmaf(cc[j], ht, yp);
+        dCv[j] = dy * ht;
+        const float lt = fmaf(dy, cc[j], lam[j]);              // lam_t
+        const float dda = lt * hp[j] * av[u][j];               // dL/d(a_t) a_t
+        ddtA = fmaf(dda, A4[j], ddtA);
+        dA[j] = fmaf(dda, dtv, dA[j]);
+        dxp = fmaf(lt, bb[j], dxp);
+        dBv[j] = lt * dtx;
+        lam[j] = av[u][j] * lt;                                // flows to t-1
+      }
+      yp = quad_sum(yp);
+      ddtA = quad_sum(ddtA);
+      dxp = quad_sum(dxp);
+      // materialise the sums here, outside the lane-masked stores below, so the last DPP
+      // step of each stays fused into its add
+      asm volatile("" : "+v"(yp), "+v"(ddtA), "+v"(dxp));
+      const float y = fmaf(Dd, xv, yp);
+      const float2 o1 = make_float2(fmaf(xv, dxp, ddtA), gz * y);     // dDelta, dz
+      const float o2 = fmaf(dxp, dtv, dy * Dd);                        // dx
+      if (q == 0) {
+        sxd[r0 + u][dl] = o1;
+        sgyb[u][dl].x = o2;
+        dDacc = fmaf(dy, xv, dDacc);
+      }
+      if (CHECK && start && dh0) st4_at(dh0 + (int64_t)iseq * dn, lo4, lam);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dBv[j] = row_channel_sum(dBv[j]);
+        dCv[j] = row_channel_sum(dCv[j]);
+      }
+      asm volatile("" : "+v"(dBv[0]), "+v"(dBv[1]), "+v"(dBv[2]), "+v"(dBv[3]));
+      asm volatile("" : "+v"(dCv[0]), "+v"(dCv[1]), "+v"(dCv[2]), "+v"(dCv[3]));
+      if ((lane & 12) == 0) {                        // channel 0 of each row: the row's sums
+        const int pr = tid >> 4;                     // row within the workgroup
+        *reinterpret_cast<float4*>(&red[u][pr][4 * q]) = make_float4(dBv[0], dBv[1], dBv[2], dBv[3]);
+        *reinterpret_cast<float4*>(&red[u][pr][NS + 4 * q]) =
+            make_float4(dCv[0], dCv[1], dCv[2], dCv[3]);
+      }
+    }
+    // one token at a time: hoisting later tokens' LDS reads would exceed the register budget
+    //__builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                      const float* __restrict__ A_log, const float* __restrict__ Bm,
                      const float* __restrict__ Cm, const float* __restrict__ Dv,
@@ -257,8 +496,11 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
   const int nsub = (nt + SUB - 1) / SUB;
   const int64_t dn = (int64_t)d_inner * NS;
   const int64_t dn4 = (int64_t)d * NS + 4 * q;   // this lane's 4 states in a (d, n) row
+  const uint32_t lo4 = (uint32_t)dn4 * 4u;       //   as a byte offset (d_inner * 64 < 2^32)
   const int su = tid >> 5;                       // copy / write-out map: token of a sub-block
   const int scp = 2 * (tid & 31);                //   and channel pair
+  const uint32_t lo_el = (uint32_t)(su * d_inner + c0 + scp);   // its element offset from the
+                                                                 // sub-block's first row
 
   // the chunk's {Delta, x}, B and C; {dy, gz} of the last sub-block
   stage_dtx<T>(sxd, dt, x, s, nt, c0, d_inner);
@@ -266,12 +508,10 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
     sbc[dl][q] = *reinterpret_cast<const float4*>(Bm + (s + dl) * NS + 4 * q);
     sbc[dl][4 + q] = *reinterpret_cast<const float4*>(Cm + (s + dl) * NS + 4 * q);
   }
-  float zr[2], gr[2];
-  fetch_zg(z, dg, s + (int64_t)(nsub - 1) * SUB + su, e, c0 + scp, d_inner, zr, gr);
-  {
-    const float2 a = dy_gz(zr[0], gr[0]), b = dy_gz(zr[1], gr[1]);
-    *reinterpret_cast<float4*>(&sgy[(nsub - 1) & 1][su][scp]) = make_float4(a.x, a.y, b.x, b.y);
-  }
+  RawZg nxt;
+  fetch_zg(z, dg, s + (int64_t)(nsub - 1) * SUB, d_inner, lo_el * (uint32_t)sizeof(T),
+           (nsub - 1) * SUB + su < nt, nxt);
+  put_gy<T>(sgy[(nsub - 1) & 1], su, scp, nxt);
   float A4[4], a2[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -288,39 +528,30 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
     int i = find_seq_b(cu, n_seqs, s);
     float h[4];
     if (cu[i] == s) {
-      if (h0) load4(h0 + (int64_t)i * dn + dn4, h); else zero4(h);
+      if (h0) ld4_at(h0 + (int64_t)i * dn, lo4, h); else zero4(h);
     } else {
-      load4(carry + (int64_t)k * dn + dn4, h);     // k >= 1 here
+      ld4_at(carry + (int64_t)k * dn, lo4, h);     // k >= 1 here
     }
     int nstart = cu[i + 1];                        // next sequence start (n_tok if none)
     for (int sb = 0; sb < nsub; ++sb) {
       const int r0 = sb * SUB;
+      const int64_t t0 = s + r0;
       const int len = nt - r0 < SUB ? nt - r0 : SUB;
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        if (u < len) {
-          if (s + r0 + u == nstart) {                // a sequence starts: its initial state
-            ++i;
-            nstart = cu[i + 1];
-            if (h0) load4(h0 + (int64_t)i * dn + dn4, h); else zero4(h);
-          }
-          if (u == 0) {
-#pragma unroll
-            for (int m = 0; m < NSUB - 1; ++m)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) ck[m][j] = ck[m + 1][j];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ck[NSUB - 1][j] = h[j];
-          }
-          const float2 v = sxd[r0 + u][dl];
-          const float4 b = sbc[r0 + u][q];
-          const float dtx = v.x * v.y;
-          h[0] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[0]), h[0], dtx * b.x);
-          h[1] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[1]), h[1], dtx * b.y);
-          h[2] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[2]), h[2], dtx * b.z);
-          h[3] = fmaf(__builtin_amdgcn_exp2f(v.x * a2[3]), h[3], dtx * b.w);
-        }
+      if (t0 == nstart) {                          // a sequence starts at the sub-block
+        ++i;
+        nstart = cu[i + 1];
+        if (h0) ld4_at(h0 + (int64_t)i * dn, lo4, h); else zero4(h);
       }
+#pragma unroll
+      for (int m = 0; m < NSUB - 1; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ck[m][j] = ck[m + 1][j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ck[NSUB - 1][j] = h[j];
+      if (len == SUB && nstart >= t0 + SUB)
+        forward_sub<false>(sxd, sbc, r0, len, t0, dl, q, a2, h, i, nstart, cu, h0, dn, lo4);
+      else
+        forward_sub<true>(sxd, sbc, r0, len, t0, dl, q, a2, h, i, nstart, cu, h0, dn, lo4);
     }
   }
 
@@ -328,9 +559,9 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
   int iseq = find_seq_b(cu, n_seqs, e - 1);               // sequence of the current token
   float lam[4];
   if (cu[iseq + 1] == e) {
-    if (dh_last) load4(dh_last + (int64_t)iseq * dn + dn4, lam); else zero4(lam);
+    if (dh_last) ld4_at(dh_last + (int64_t)iseq * dn, lo4, lam); else zero4(lam);
   } else {
-    load4(Iin + (int64_t)k * dn + dn4, lam);
+    ld4_at(Iin + (int64_t)k * dn, lo4, lam);
   }
   float dA[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   float dDacc = 0.0f;
@@ -339,8 +570,7 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
     const int r0 = sb * SUB;
     const int64_t t0 = s + r0;
     const int len = nt - r0 < SUB ? nt - r0 : SUB;
-    if (sb > 0) fetch_zg(z, dg, t0 - SUB + su, e, c0 + scp, d_inner, zr, gr);
-    // hq[u + 1] = state after token u, hq[0] = state entering the sub-block; av = decays
+    if (sb > 0) fetch_zg(z, dg, t0 - SUB, d_inner, lo_el * (uint32_t)sizeof(T), true, nxt);
     float hq[SUB + 1][4], av[SUB][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) hq[0][j] = ck[NSUB - 1][j];
@@ -348,119 +578,47 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
     for (int m = NSUB - 1; m > 0; --m)
 #pragma unroll
       for (int j = 0; j < 4; ++j) ck[m][j] = ck[m - 1][j];
-    {
+    // sequence of the sub-block's last token; a full sub-block inside one sequence takes the
+    // path without per-token boundary checks
+    int il = iseq;
+    while (cu[il] > t0 + len - 1) --il;
+    if (len == SUB && cu[il] <= t0) {
+      iseq = il;
+      if (t0 + SUB < e && cu[il + 1] == t0 + SUB) {       // its last token ends the sequence
+        if (dh_last) ld4_at(dh_last + (int64_t)il * dn, lo4, lam); else zero4(lam);
+      }
+      recompute_sub<false>(sxd, sbc, r0, len, t0, dl, q, a2, hq, av, il, cu, h0, dn, lo4);
+      reverse_sub<false>(sxd, sgy[p], sbc, red, r0, len, t0, e, dl, q, lane, tid, hq, av, A4,
+                         Dd, lam, dA, dDacc, iseq, cu, h0, dh_last, dh0, dn, lo4);
+      if (cu[il] == t0 && dh0) st4_at(dh0 + (int64_t)il * dn, lo4, lam);
+    } else {
       int ii = iseq;
       while (cu[ii] > t0) --ii;
-      int ns = cu[ii + 1];
-      float hh[4] = {hq[0][0], hq[0][1], hq[0][2], hq[0][3]};
-#pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        if (u < len) {
-          if (u > 0 && t0 + u == ns) {               // a sequence starts inside
-            ++ii;
-            ns = cu[ii + 1];
-            if (h0) load4(h0 + (int64_t)ii * dn + dn4, hh); else zero4(hh);
-          }
-          const float2 v = sxd[r0 + u][dl];
-          const float4 b = sbc[r0 + u][q];
-          const float dtx = v.x * v.y;
-          const float bb[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            av[u][j] = __builtin_amdgcn_exp2f(v.x * a2[j]);
-            hh[j] = fmaf(av[u][j], hh[j], dtx * bb[j]);
-            hq[u + 1][j] = hh[j];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = SUB - 1; u >= 0; --u) {
-      if (u < len) {
-        const int64_t t = t0 + u;
-        while (cu[iseq] > t) --iseq;                      // sequence of token t
-        // t ends its sequence inside the chunk: nothing arrives from the next sequence
-        // (the chunk's last token got its incoming adjoint before the loop)
-        if (t + 1 == cu[iseq + 1] && t + 1 < e) {
-          if (dh_last) load4(dh_last + (int64_t)iseq * dn + dn4, lam); else zero4(lam);
-        }
-        const bool start = t == cu[iseq];
-        float hp[4];
-        if (start && u > 0) {                             // state before t: the initial one
-          if (h0) load4(h0 + (int64_t)iseq * dn + dn4, hp); else zero4(hp);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) hp[j] = hq[u][j];
-        }
-        const float2 v = sxd[r0 + u][dl];
-        const float2 gy = sgy[p][u][dl];
-        const float4 b4 = sbc[r0 + u][q];
-        const float4 c4 = sbc[r0 + u][4 + q];
-        const float dtv = v.x, xv = v.y, dy = gy.x, gz = gy.y;
-        const float dtx = dtv * xv;
-        const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w};
-        float yp = 0.0f, ddtA = 0.0f, dxp = 0.0f;
-        float dBv[4], dCv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float ht = hq[u + 1][j];
-          yp = fmaf(cc[j], ht, yp);
-          dCv[j] = dy * ht;
-          const float lt = fmaf(dy, cc[j], lam[j]);              // lam_t
-          const float dda = lt * hp[j] * av[u][j];               // dL/d(a_t) a_t
-          ddtA = fmaf(dda, A4[j], ddtA);
-          dA[j] = fmaf(dda, dtv, dA[j]);
-          dxp = fmaf(lt, bb[j], dxp);
-          dBv[j] = lt * dtx;
-          lam[j] = av[u][j] * lt;                                // flows to t-1
-        }
-        yp = quad_sum(yp);
-        ddtA = quad_sum(ddtA);
-        dxp = quad_sum(dxp);
-        if (q == 0) {
-          const float y = fmaf(Dd, xv, yp);
-          sxd[r0 + u][dl] = make_float2(fmaf(xv, dxp, ddtA), gz * y);   // dDelta, dz
-          sgy[p][u][dl].x = fmaf(dxp, dtv, dy * Dd);                     // dx
-          dDacc = fmaf(dy, xv, dDacc);
-        }
-        if (start && dh0) store4(dh0 + (int64_t)iseq * dn + dn4, lam);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dBv[j] = row_channel_sum(dBv[j]);
-          dCv[j] = row_channel_sum(dCv[j]);
-        }
-        if ((lane & 12) == 0) {                        // channel 0 of each row: the row's sums
-          const int pr = tid >> 4;                     // row within the workgroup
-          *reinterpret_cast<float4*>(&red[u][pr][4 * q]) = make_float4(dBv[0], dBv[1], dBv[2], dBv[3]);
-          *reinterpret_cast<float4*>(&red[u][pr][NS + 4 * q]) =
-              make_float4(dCv[0], dCv[1], dCv[2], dCv[3]);
-        }
-      }
+      recompute_sub<true>(sxd, sbc, r0, len, t0, dl, q, a2, hq, av, ii, cu, h0, dn, lo4);
+      reverse_sub<true>(sxd, sgy[p], sbc, red, r0, len, t0, e, dl, q, lane, tid, hq, av, A4,
+                        Dd, lam, dA, dDacc, iseq, cu, h0, dh_last, dh0, dn, lo4);
     }
     __syncthreads();
     // write-out: dB | dC partial of the workgroup (thread = token su, value tid % 32) and the
     // sub-block's dx, dDelta, dz rows (thread = token su, channels scp, scp + 1)
     if (su < len) {
-      const int64_t t = t0 + su;
-      const int v = tid & 31;
       float sum = 0.0f;
 #pragma unroll
-      for (int pr = 0; pr < 16; ++pr) sum += red[su][pr][v];
-      dBC_part[((int64_t)blockIdx.x * n_tok + t) * (2 * NS) + v] = sum;
+      for (int pr = 0; pr < 16; ++pr) sum += red[su][pr][tid & 31];
+      // thread tid writes value tid % 32 of token su: offset tid from the sub-block's first row
+      st1_at(dBC_part + ((int64_t)blockIdx.x * n_tok + t0) * (2 * NS), (uint32_t)tid * 4u, sum);
       const float4 o1 = *reinterpret_cast<const float4*>(&sxd[r0 + su][scp]);
       const float4 o2 = *reinterpret_cast<const float4*>(&sgy[p][su][scp]);
-      const int64_t o = t * d_inner + c0 + scp;
-      *reinterpret_cast<float2*>(ddt + o) = make_float2(o1.x, o1.z);
-      *reinterpret_cast<float2*>(dz + o) = make_float2(o1.y, o1.w);
-      *reinterpret_cast<float2*>(dx + o) = make_float2(o2.x, o2.z);
+      const int64_t row = t0 * d_inner;
+      const uint32_t lo = lo_el * 4u;
+      st2_at(ddt + row, lo, o1.x, o1.z);
+      st2_at(dz + row, lo, o1.y, o1.w);
+      st2_at(dx + row, lo, o2.x, o2.z);
     }
-    if (sb > 0) {                                      // {dy, gz} of the next sub-block
-      const float2 a = dy_gz(zr[0], gr[0]), b = dy_gz(zr[1], gr[1]);
-      *reinterpret_cast<float4*>(&sgy[p ^ 1][su][scp]) = make_float4(a.x, a.y, b.x, b.y);
-    }
+    if (sb > 0) put_gy<T>(sgy[p ^ 1], su, scp, nxt);   // {dy, gz} of the next sub-block
     __syncthreads();
   }
-  store4(dA_part + (int64_t)k * dn + dn4, dA);
+  st4_at(dA_part + (int64_t)k * dn, lo4, dA);
   if (q == 0) dD_part[(int64_t)k * d_inner + d] = dDacc;
 }
 

@@ -126,10 +126,24 @@ void scan_chunk_carry_kernel(const float* __restrict__ agg_P, const float* __res
   // chunk's aggregate is never produced.
   float c = 0.0f;
   carry[dn] = c;
-  for (int k = 1; k < n_chunks; ++k) {
-    const int64_t prev = (int64_t)(k - 1) * dn_count + dn;
-    c = fmaf(agg_P[prev], c, agg_h[prev]);
-    carry[(int64_t)k * dn_count + dn] = c;
+  // eight chunks per step: their aggregates are loaded before the chain uses them, so the
+  // loads of a step are in flight together (the chain itself is one FMA per chunk)
+  constexpr int U = 8;
+  for (int k0 = 1; k0 < n_chunks; k0 += U) {
+    float P[U], h[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t prev = (int64_t)(k0 + u - 1) * dn_count + dn;
+      P[u] = k0 + u < n_chunks ? agg_P[prev] : 0.0f;
+      h[u] = k0 + u < n_chunks ? agg_h[prev] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u < n_chunks) {
+        c = fmaf(P[u], c, h[u]);
+        carry[(int64_t)(k0 + u) * dn_count + dn] = c;
+      }
+    }
   }
 }
 

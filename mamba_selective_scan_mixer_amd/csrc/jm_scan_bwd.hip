@@ -255,12 +255,25 @@ void bwd_carry_kernel(const float* __restrict__ Lin, const float* __restrict__ P
   if (idx >= dn) return;
   float I = 0.0f;
   Iin[(int64_t)(n_chunks - 1) * dn + idx] = 0.0f;
-  for (int k = n_chunks - 1; k >= 1; --k) {
-    // I = adjoint entering chunk k at its end; chunk k passes P_k I + L_k to chunk k-1
-    // (P_{K-1} is never needed: I is 0 there)
-    const float p = k < n_chunks - 1 ? P[(int64_t)k * dn + idx] : 0.0f;
-    I = fmaf(p, I, Lin[(int64_t)k * dn + idx]);
-    Iin[(int64_t)(k - 1) * dn + idx] = I;
+  // I = adjoint entering chunk k at its end; chunk k passes P_k I + L_k to chunk k-1
+  // (P_{K-1} is never needed: I is 0 there). Eight chunks per step, loads first.
+  constexpr int U = 8;
+  for (int k0 = n_chunks - 1; k0 >= 1; k0 -= U) {
+    float p[U], l[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 - u;
+      p[u] = k >= 1 && k < n_chunks - 1 ? P[(int64_t)k * dn + idx] : 0.0f;
+      l[u] = k >= 1 ? Lin[(int64_t)k * dn + idx] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 - u;
+      if (k >= 1) {
+        I = fmaf(p[u], I, l[u]);
+        Iin[(int64_t)(k - 1) * dn + idx] = I;
+      }
+    }
   }
 }
 
@@ -628,32 +641,51 @@ void bwd_reduce_bc_kernel(const float* __restrict__ part, float* __restrict__ dB
                           float* __restrict__ dC, int n_cblocks, int64_t n_tok) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;   // token * 32 + value
   if (idx >= n_tok * 2 * NS) return;
-  float sum = 0.0f;
-  for (int cb = 0; cb < n_cblocks; ++cb) sum += part[(int64_t)cb * n_tok * 2 * NS + idx];
+  // eight running sums (channel blocks cb = u mod 8), combined pairwise: fixed order
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c0 = 0; c0 < n_cblocks; c0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c0 + u < n_cblocks) acc[u] += part[(int64_t)(c0 + u) * n_tok * 2 * NS + idx];
+  }
+  const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   const int64_t t = idx / (2 * NS);
   const int v = (int)(idx % (2 * NS));
   if (v < NS) dB[t * NS + v] = sum;
   else dC[t * NS + (v - NS)] = sum;
 }
 
+// dA_log and dD: sums over the chunks' partials. Workgroup = 64 consecutive entries; wave w
+// sums chunks w, w + 4, w + 8, ... with eight running sums (eight loads in flight), and the
+// four waves' sums are added in LDS in a fixed order.
 __global__ __launch_bounds__(256)
 void bwd_reduce_param_kernel(const float* __restrict__ dA_part, const float* __restrict__ dD_part,
                              const float* __restrict__ A_log, float* __restrict__ dA_log,
                              float* __restrict__ dD, int n_chunks, int d_inner) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float part[4][64];
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const int64_t dn = (int64_t)d_inner * NS;
-  if (idx < dn) {
-    float sum = 0.0f;
-    for (int k = 0; k < n_chunks; ++k) sum += dA_part[(int64_t)k * dn + idx];
-    dA_log[idx] = -fast_exp(A_log[idx]) * sum;     // dA/dA_log = A
+  const int64_t nA = dn / 64;                           // workgroups for dA_log
+  const bool isA = blockIdx.x < nA;
+  const int64_t idx = (isA ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - nA) * 64 + l;
+  const float* src = isA ? dA_part : dD_part;
+  const int64_t stride = isA ? dn : d_inner;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = w; k0 < n_chunks; k0 += 32) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = k0 + 4 * u;
+      if (k < n_chunks) acc[u] += src[(int64_t)k * stride + idx];
+    }
   }
-  if (idx < d_inner) {
-    float sum = 0.0f;
-    for (int k = 0; k < n_chunks; ++k) sum += dD_part[(int64_t)k * d_inner + idx];
-    dD[idx] = sum;
+  part[w][l] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  __syncthreads();
+  if (w == 0) {
+    const float sum = (part[0][l] + part[1][l]) + (part[2][l] + part[3][l]);
+    if (isA) dA_log[idx] = -fast_exp(A_log[idx]) * sum;   // dA/dA_log = A
+    else dD[idx] = sum;
   }
 }
-
 }  // namespace
 
 size_t scan_backward_workspace_floats(int64_t n_tok, int d_inner) {
@@ -719,9 +751,9 @@ hipError_t launch_scan_bwd_reduce(const ScanBwdLayout& w, const float* A_log, in
                      w.bc_part, dB, dC, d_inner / BW_CH, n_tok);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t dn = (int64_t)d_inner * NS;
-  hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((dn + 255) / 256)), dim3(256), 0, s,
-                     w.dA_part, w.dD_part, A_log, dA_log, dD, w.K, d_inner);
+  const int64_t dn = (int64_t)d_inner * NS;   // d_inner % 64 == 0: whole workgroups
+  hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((dn + d_inner) / 64)), dim3(256), 0,
+                     s, w.dA_part, w.dD_part, A_log, dA_log, dD, w.K, d_inner);
   return hipGetLastError();
 }
 

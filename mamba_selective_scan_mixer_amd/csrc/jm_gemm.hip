@@ -241,18 +241,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 // no index stride).
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
-// Chunk position of 16-byte chunk 0 of row r in a 32-column (64-byte) LDS row.
-__device__ __forceinline__ int swz32(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// Chunk position of 16-byte chunk 0 of row r in a 64-column (128-byte) LDS row: the 16 lanes
+// an LDS read serves together (rows r0..r0+15, one chunk column) then hit 16 distinct 16-byte
+// bank groups (even rows take chunk positions 0..7 in the first 64 bytes of the bank window,
+// odd rows in the second).
+__device__ __forceinline__ int swz64(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <int CNT>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
 }
 
-constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 4, MS_WN = 2, MS_S = 4, MS_BK = 32;
-constexpr int MS_LDS_BYTES = MS_S * (MS_BM + MS_BN) * MS_BK * 2;
+// 256 x 256 tiles, 8 waves, K slices of 64 (128-byte row segments: one L2 request per row per
+// slice, half the requests of 64-byte segments), two LDS buffers of 64 KB.
+constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 4, MS_WN = 2, MS_BK = 64;
+constexpr int MS_LDS_BYTES = 2 * (MS_BM + MS_BN) * MS_BK * 2;
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int S, int BKC, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BKC, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ W,
@@ -265,12 +270,11 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   constexpr int RPI = 64 / CPR;              // rows written by one 1 KB DMA instruction
   constexpr int XI = BM / RPI / NW;          // DMA instructions per wave per stage (X)
   constexpr int WI = BN / RPI / NW;          // (W)
-  constexpr int LPS = XI + WI;
   constexpr int SPS = BKC / 16;              // k16 steps per stage
   constexpr int STAGE = (BM + BN) * BKC;     // bf16 elements per stage
   constexpr int NM = FN * FM;                // MFMAs per k16 step
   constexpr int NR = FN + FM;                // fragment reads per k16 step
-  static_assert(BKC == 32 && SPS == 2 && XI >= 1 && WI >= 1 && S >= 3, "tiling");
+  static_assert(BKC == 64 && SPS == 4 && XI >= 1 && WI >= 1 && NM % 2 == 0, "tiling");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   bf16* lds = reinterpret_cast<bf16*>(smem);
 
@@ -288,13 +292,12 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // Rows past M / N are clamped to the last row (their results are never stored).
   // The loads are buffer loads: one descriptor per operand whose base is the tile's first
   // row, a fixed 32-bit byte offset per lane and instruction, and the k advance in the
-  // scalar offset (the host checks that 256 rows + K fit 2^31 bytes). Their per-lane
-  // address is half the size of a global load's, which measured ~2% faster here.
+  // scalar offset (the host checks that 256 rows + K fit 2^31 bytes).
   uint32_t xoff[XI], woff[WI];
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
     const int row = (wave * XI + i) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz32(row);
+    const int c = (lane % CPR) ^ swz64(row);
     int64_t r = row;
     if (m0 + r >= M) r = M - 1 - m0;
     xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
@@ -302,7 +305,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int row = (wave * WI + i) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz32(row);
+    const int c = (lane % CPR) ^ swz64(row);
     int64_t r = row;
     if (n0 + r >= N) r = N - 1 - n0;
     woff[i] = (uint32_t)((r * ldw + c * 8) * 2);
@@ -313,23 +316,28 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + (int64_t)n0 * ldw), (short)0, 0x7fffffff, kBufferRsrcWord3);
 #endif
-  auto issue = [&](int kt, int buf) {
+  // the X half and the W half of a stage's DMA, issued at different points of the loop
+  auto issue_x = [&](int kt, int buf) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const int kb = kt * BKC * 2;
     char* base = reinterpret_cast<char*>(lds + buf * STAGE);
 #pragma unroll
     for (int i = 0; i < XI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(base + (wave * XI + i) * 1024), 16,
-                                               xoff[i], kb, 0, 0);
+                                               xoff[i], kt * BKC * 2, 0, 0);
+#endif
+  };
+  auto issue_w = [&](int kt, int buf) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    char* base = reinterpret_cast<char*>(lds + buf * STAGE) + BM * BKC * 2;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr, (lds_void*)(base + BM * BKC * 2 + (wave * WI + i) * 1024), 16, woff[i], kb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(base + (wave * WI + i) * 1024), 16,
+                                               woff[i], kt * BKC * 2, 0, 0);
 #endif
   };
   const int lrow = lane & 31;
   const int khalf = lane >> 5;
-  const int sw = swz32(lrow);   // equal for all fragment rows of a lane (they differ by 32s)
+  const int sw = swz64(lrow);   // equal for all fragment rows of a lane (they differ by 32s)
   int offW[FN], offX[FM];
 #pragma unroll
   for (int a = 0; a < FN; ++a) offW[a] = BM * BKC + (wn0 + a * 32 + lrow) * BKC;
@@ -360,58 +368,88 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
     }
   };
 
+  // Two buffers: stage kt lives in buffer kt & 1. The barrier that ends stage kt frees its
+  // buffer; the X half of stage kt+2 goes there at once, the W half during stage kt+1's first
+  // k16 step; both are waited for (vmcnt 0) before the barrier that ends stage kt+1.
   const int nk = K / BKC;
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st)
-    if (st < nk) issue(st, st);
-  if (nk >= S - 1) wait_vmcnt<(S - 2) * LPS>(); else wait_vmcnt<0>();
+  issue_x(0, 0);
+  issue_w(0, 0);
+  if (nk > 1) {
+    issue_x(1, 1);
+    wait_vmcnt<XI>();     // stage 0 complete; stage 1's X half may be in flight
+  } else {
+    wait_vmcnt<0>();
+  }
   __builtin_amdgcn_s_barrier();
   load_frags(0, 0, fw[0], fx[0]);
-  int rbuf = 0;      // stage being computed
-  int wbuf = S - 1;  // stage the next DMA fills
   int kt = 0;
-  // Steady state: no conditionals, so the compiler counts outstanding LDS reads exactly.
-  for (; kt + S - 1 < nk; ++kt) {
-    // k16 step 0: fetch step 1's fragments under step 0's MFMAs
-    load_frags(rbuf, 1, fw[1], fx[1]);
-    mfma_range(0, 0, NM);
+  // Steady state (stages kt+1 and kt+2 exist): no conditionals, so the compiler counts
+  // outstanding LDS reads exactly.
+  for (; kt + 2 < nk; ++kt) {
+    const int rb = kt & 1;
 #pragma unroll
-    for (int q = 0; q < NR; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-    // k16 step 1: half its MFMAs, then the stage barrier, the next DMA and the
-    // next stage's first fragments, interleaved with the other half
-    mfma_range(1, 0, NM / 2);
-    __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
-    wait_vmcnt<(S - 3) * LPS>();
-    __builtin_amdgcn_s_barrier();
-    issue(kt + S - 1, wbuf);
-    const int nbuf = (rbuf + 1 == S) ? 0 : rbuf + 1;
-    load_frags(nbuf, 0, fw[0], fx[0]);
-    mfma_range(1, NM / 2, NM);
+    for (int s = 0; s < SPS; ++s) {
+      const int cur = s & 1;
+      if (s == 0) {
+        issue_w(kt + 1, rb ^ 1);
+        load_frags(rb, 1, fw[1], fx[1]);
+        mfma_range(0, 0, NM);
 #pragma unroll
-    for (int q = 0; q < NM / 2; ++q) {
-      if (q < LPS) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // 1 DMA
-      if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int q = 0; q < NM; ++q) {
+          if (q < WI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
+          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+        }
+      } else if (s + 1 < SPS) {
+        load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
+        mfma_range(cur, 0, NM);
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+      } else {
+        // half the MFMAs, the stage barrier, then the X DMA of stage kt+2 and the next
+        // stage's first fragments under the other half
+        mfma_range(cur, 0, NM / 2);
+        __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        issue_x(kt + 2, rb);
+        load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
+        mfma_range(cur, NM / 2, NM);
+        constexpr int DPS = (XI + NM / 2 - 1) / (NM / 2);   // DMAs per MFMA slot
+        constexpr int RPS = (NR + NM / 2 - 1) / (NM / 2);   // reads per MFMA slot
+#pragma unroll
+        for (int q = 0; q < NM / 2; ++q) {
+#pragma unroll
+          for (int z = 0; z < DPS; ++z)
+            if (q * DPS + z < XI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+          for (int z = 0; z < RPS; ++z)
+            if (q * RPS + z < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      }
     }
-    rbuf = nbuf;
-    wbuf = (wbuf + 1 == S) ? 0 : wbuf + 1;
   }
-  // Drain: the last S-1 stages are already in flight.
+  // Last two stages (nothing more to load after stage kt+1's W half).
   for (; kt < nk; ++kt) {
-    load_frags(rbuf, 1, fw[1], fx[1]);
-    mfma_range(0, 0, NM);
-    const int nbuf = (rbuf + 1 == S) ? 0 : rbuf + 1;
-    if (kt + 1 < nk) {
-      wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      load_frags(nbuf, 0, fw[0], fx[0]);
+    const int rb = kt & 1;
+#pragma unroll
+    for (int s = 0; s < SPS; ++s) {
+      const int cur = s & 1;
+      if (s == 0 && kt + 1 < nk) issue_w(kt + 1, rb ^ 1);
+      if (s + 1 < SPS) {
+        load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
+      } else if (kt + 1 < nk) {
+        wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
+      }
+      mfma_range(cur, 0, NM);
     }
-    mfma_range(1, 0, NM);
-    rbuf = nbuf;
   }
 
   // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
@@ -584,7 +622,7 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
     const int tiles_n = (N + MS_BN - 1) / MS_BN;
     const int64_t n_wg = tiles_m * tiles_n;
     if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
-    auto kern = gemm_bf16_kernel<MS_BM, MS_BN, MS_WM, MS_WN, MS_S, MS_BK, EPI>;
+    auto kern = gemm_bf16_kernel<MS_BM, MS_BN, MS_WM, MS_WN, MS_BK, EPI>;
     static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled once
     if (!attr_set) {
       hipError_t e = hipFuncSetAttribute((const void*)kern,

@@ -153,37 +153,89 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
   __syncthreads();
   // FB x 2 x 16 x 64 outputs; block (f, tb), register r, lane l:
   // feature n0 + 32 f + 8(r/4) + 4(l/32) + r%4, token l%32 + 32 tb.
-  for (int o = threadIdx.x; o < FB * 2048; o += 64 * WAVES) {
-    const int blk = o >> 10, r = (o >> 6) & 15, l = o & 63;
-    const int f = blk >> 1, tb = blk & 1;
-    float v = 0.0f;
+  // Write-out by items of one token and 8 consecutive features (16-byte loads and stores):
+  // item (m, g) covers features n0 + 8g .. +7, i.e. f = g/4, r = 4(g%4) + c%4 and
+  // l = m%32 + 32(c/4) for feature c of the item. All of an item's global loads are issued
+  // before any is used, and a thread's items are independent, so the write-out costs about
+  // one memory latency rather than one per output.
+  constexpr int ITEMS = 64 * NB / 8;
+  constexpr int IPT = (ITEMS + 64 * WAVES - 1) / (64 * WAVES);
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) v += red[w][blk][r][l];
-    const int m = (l & 31) + 32 * tb;
-    const int n = n0 + 32 * f + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+  for (int it = 0; it < IPT; ++it) {
+    const int item = threadIdx.x + it * 64 * WAVES;
+    if (item >= ITEMS) break;
+    const int m = item / (NB / 8), g = item % (NB / 8);
+    const int f = g >> 2, q = g & 3, tb = m >> 5;
+    const int n = n0 + 8 * g;
     if (m >= M || n >= N) continue;
+    float v[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int r = 4 * q + (c & 3), l = (m & 31) + 32 * (c >> 2);
+      float a = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) a += red[w][2 * f + tb][r][l];
+      v[c] = a;
+    }
+    const bool whole = n + 8 <= N;
     if constexpr (EPI == DEC_STORE) {
-      e.out[(int64_t)m * N + n] = from_f32<bf16>(v);
+      if (whole) {
+        bf16x8 o;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(v[c]);
+        *reinterpret_cast<bf16x8*>(e.out + (int64_t)m * N + n) = o;
+      } else {
+        for (int c = 0; c < 8 && n + c < N; ++c) e.out[(int64_t)m * N + n + c] = from_f32<bf16>(v[c]);
+      }
     } else if constexpr (EPI == DEC_PARTIAL) {
-      e.partial[((int64_t)split * M + m) * N + n] = v;
+      float* dst = e.partial + ((int64_t)split * M + m) * N + n;
+      if (whole) {
+        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        for (int c = 0; c < 8 && n + c < N; ++c) dst[c] = v[c];
+      }
     } else {
+      // in_proj: features < d_inner are x (conv-state shift, conv, SiLU), the rest z.
+      // d_inner % 64 == 0, so an item is entirely x or entirely z.
       const int di = e.d_inner;
       if (n < di) {
-        bf16* st = e.conv_state + ((e.rows ? (int64_t)e.rows[m] : (int64_t)m) * di + n) * 3;
-        const bf16 xb = from_f32<bf16>(v);
-        const float s0 = to_f32(st[0]), s1 = to_f32(st[1]), s2 = to_f32(st[2]);
-        const bf16* cw = e.conv_w + (int64_t)n * 4;
-        float c = e.conv_b ? to_f32(e.conv_b[n]) : 0.0f;
-        c = fmaf(to_f32(cw[0]), s0, c);
-        c = fmaf(to_f32(cw[1]), s1, c);
-        c = fmaf(to_f32(cw[2]), s2, c);
-        c = fmaf(to_f32(cw[3]), to_f32(xb), c);
-        e.xh[(int64_t)m * di + n] = from_f32<bf16>(silu(c));
-        st[0] = st[1];
-        st[1] = st[2];
-        st[2] = xb;
+        const int64_t row = e.rows ? (int64_t)e.rows[m] : (int64_t)m;
+        bf16x8* st = reinterpret_cast<bf16x8*>(e.conv_state + (row * di + n) * 3);   // 48 bytes
+        const bf16x8* cw = reinterpret_cast<const bf16x8*>(e.conv_w + (int64_t)n * 4);  // 64 bytes
+        bf16x8 s3[3], w4[4], b8;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) s3[k] = st[k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w4[k] = cw[k];
+        if (e.conv_b) b8 = *reinterpret_cast<const bf16x8*>(e.conv_b + n);
+        bf16x8 xo, so[3];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          // state of feature n + c: elements 3c .. 3c+2 of the 24 (oldest first);
+          // taps of feature n + c: elements 4c .. 4c+3 of the 32
+          const float h0 = to_f32(s3[(3 * c) >> 3][(3 * c) & 7]);
+          const float h1 = to_f32(s3[(3 * c + 1) >> 3][(3 * c + 1) & 7]);
+          const float h2 = to_f32(s3[(3 * c + 2) >> 3][(3 * c + 2) & 7]);
+          const bf16 xb = from_f32<bf16>(v[c]);
+          float acc = e.conv_b ? to_f32(b8[c]) : 0.0f;
+          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1)]), h0, acc);
+          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 1]), h1, acc);
+          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 2]), h2, acc);
+          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 3]), to_f32(xb), acc);
+          xo[c] = from_f32<bf16>(silu(acc));
+          so[(3 * c) >> 3][(3 * c) & 7] = s3[(3 * c + 1) >> 3][(3 * c + 1) & 7];
+          so[(3 * c + 1) >> 3][(3 * c + 1) & 7] = s3[(3 * c + 2) >> 3][(3 * c + 2) & 7];
+          so[(3 * c + 2) >> 3][(3 * c + 2) & 7] = xb;
+        }
+        *reinterpret_cast<bf16x8*>(e.xh + (int64_t)m * di + n) = xo;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) st[k] = so[k];
       } else {
-        e.z[(int64_t)m * di + (n - di)] = from_f32<bf16>(v);
+        bf16x8 o;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(v[c]);
+        *reinterpret_cast<bf16x8*>(e.z + (int64_t)m * di + (n - di)) = o;
       }
     }
   }

@@ -275,6 +275,8 @@ void dec_xproj_reduce_kernel(const float* __restrict__ partial, int splits, int 
 // one token at a time, with its 16 states in registers (four 16-byte loads in flight).
 constexpr int UPD_CH = 32;
 constexpr int UPD_MT = 32;
+// KQ: each wave's share of dt_rank when known at compile time (0: dt_rank / 4 at run time)
+template <int KQ>
 __global__ __launch_bounds__(256)
 void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
                        const bf16* __restrict__ delta, const float* __restrict__ Bm,
@@ -284,65 +286,112 @@ void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
                        const int32_t* __restrict__ rows, bf16* __restrict__ g, int M,
                        int d_inner, int R) {
   __shared__ float sdt[4][UPD_MT][UPD_CH + 1];
+  __shared__ float4 sbc[UPD_MT][8];         // B_t (4 float4) | C_t (4 float4) of the tile's tokens
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int d0 = blockIdx.x * UPD_CH;
   const int m0 = blockIdx.y * UPD_MT;
+  const int mend = min(M - m0, UPD_MT);
+  const int c = lane & (UPD_CH - 1);
+  const int d = d0 + c;
+  // Everything that does not depend on dt_proj is requested first, so its latency overlaps
+  // the dt_proj MFMAs and the barrier: B|C of the tile's tokens (staged into LDS after the
+  // MFMAs), A, D, the bias, the state rows and then every state row, x and z of this thread's
+  // tokens (ml0, ml0 + 8, ...). A token past the batch reads token m0's rows instead and its
+  // results are dropped. State rows of a batch are distinct: the host rejects a slot that
+  // appears twice, and without a slot map row m is token m.
+  const int t_bc = threadIdx.x >> 3, part = threadIdx.x & 7;
+  float4 bcv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (t_bc < mend)
+    bcv = *reinterpret_cast<const float4*>((part < 4 ? Bm : Cm) + (int64_t)(m0 + t_bc) * NS +
+                                           4 * (part & 3));
+  float a2[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) a2[n] = A_log[(int64_t)d * NS + n];
+  const float Dd = Dv[d];
+  const float bias = b_dt[d];
+  constexpr int TPT = UPD_MT / 8;           // tokens per thread
+  const int ml0 = (wave << 1) | (lane >> 5);
+  int64_t srow[TPT];
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    const int m = ml0 + 8 * j < mend ? m0 + ml0 + 8 * j : m0;
+    srow[j] = rows ? (int64_t)rows[m] : (int64_t)m;
+  }
   {
+    // dt_proj on MFMA: this wave sums a quarter of dt_rank; all its fragments are fetched
+    // before the first MFMA (dt_rank <= 256 here: at most 4 k-steps per wave)
     const int lrow = lane & 31, half = lane >> 5;
     const int tok = m0 + lrow;              // rows >= M read row 0; their results are unused
-    const int kq = R / 4;                   // this wave's share of dt_rank
+    const int kq = KQ ? KQ : R / 4;          // this wave's share of dt_rank (multiple of 32)
     const bf16* dp = delta + (int64_t)(tok < M ? tok : 0) * R + wave * kq + 8 * half;
     const bf16* wp = W_dt + (int64_t)(d0 + lrow) * R + wave * kq + 8 * half;
     f32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    for (int kk = 0; kk < kq; kk += 16) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(dp + kk);
-      const bf16x8 w = *reinterpret_cast<const bf16x8*>(wp + kk);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, a, acc, 0, 0, 0);
+    for (int kk = 0; kk < kq; kk += 64) {
+      bf16x8 a[4], w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int k = kk + 16 * u < kq ? kk + 16 * u : kk;   // past kq: a repeat, not used
+        a[u] = *reinterpret_cast<const bf16x8*>(dp + k);
+        w[u] = *reinterpret_cast<const bf16x8*>(wp + k);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (kk + 16 * u < kq) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[u], a[u], acc, 0, 0, 0);
     }
     // acc row = channel, column = token
 #pragma unroll
     for (int r = 0; r < 16; ++r) sdt[wave][lrow][8 * (r >> 2) + 4 * half + (r & 3)] = acc[r];
   }
-  __syncthreads();
-  const int c = lane & (UPD_CH - 1);
-  const int d = d0 + c;
-  float a2[NS];
+  float h[TPT][NS], xv[TPT], zv[TPT];
 #pragma unroll
-  for (int n = 0; n < NS; ++n) a2[n] = -fast_exp(A_log[(int64_t)d * NS + n]) * kLog2e;
-  const float Dd = Dv[d];
-  const float bias = b_dt[d];
-  const int mend = min(M - m0, UPD_MT);
-  for (int ml = (wave << 1) | (lane >> 5); ml < mend; ml += 8) {
-    const int m = m0 + ml;
+  for (int j = 0; j < TPT; ++j) {
+    const int m = ml0 + 8 * j < mend ? m0 + ml0 + 8 * j : m0;
     const int64_t o = (int64_t)m * d_inner + d;
-    const float dtv =
-        softplus(((sdt[0][ml][c] + sdt[1][ml][c]) + (sdt[2][ml][c] + sdt[3][ml][c])) + bias);
-    const float xv = to_f32(xh[o]);
-    const float zv = to_f32(z[o]);
-    const float dx = dtv * xv;
-    const int64_t so = (rows ? (int64_t)rows[m] : (int64_t)m) * d_inner + d;
-    float4* st = reinterpret_cast<float4*>(state + so * NS);
-    float h[NS];
+    xv[j] = to_f32(xh[o]);
+    zv[j] = to_f32(z[o]);
+    const float4* st = reinterpret_cast<const float4*>(state + (srow[j] * d_inner + d) * NS);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 f = st[q];
-      h[4 * q] = f.x; h[4 * q + 1] = f.y; h[4 * q + 2] = f.z; h[4 * q + 3] = f.w;
+      h[j][4 * q] = f.x; h[j][4 * q + 1] = f.y; h[j][4 * q + 2] = f.z; h[j][4 * q + 3] = f.w;
     }
-    const float* bb = Bm + m * NS;
-    const float* cc = Cm + m * NS;
-    float y = 0.0f;
+  }
+  if (t_bc < mend) sbc[t_bc][part] = bcv;
+  __syncthreads();
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      h[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[n], dx * bb[n]);
-      y = fmaf(cc[n], h[n], y);
+  for (int n = 0; n < NS; ++n) a2[n] = -fast_exp(a2[n]) * kLog2e;
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    const int ml = ml0 + 8 * j;
+    if (ml < mend) {
+      const int m = m0 + ml;
+      const int64_t o = (int64_t)m * d_inner + d;
+      const float dtv =
+          softplus(((sdt[0][ml][c] + sdt[1][ml][c]) + (sdt[2][ml][c] + sdt[3][ml][c])) + bias);
+      const float dx = dtv * xv[j];
+      float bb[NS], cc[NS];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 b4 = sbc[ml][q], c4 = sbc[ml][4 + q];
+        bb[4 * q] = b4.x; bb[4 * q + 1] = b4.y; bb[4 * q + 2] = b4.z; bb[4 * q + 3] = b4.w;
+        cc[4 * q] = c4.x; cc[4 * q + 1] = c4.y; cc[4 * q + 2] = c4.z; cc[4 * q + 3] = c4.w;
+      }
+      float y = 0.0f;
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        h[j][n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[j][n], dx * bb[n]);
+        y = fmaf(cc[n], h[j][n], y);
+      }
+      float4* st = reinterpret_cast<float4*>(state + (srow[j] * d_inner + d) * NS);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        st[q] = make_float4(h[j][4 * q], h[j][4 * q + 1], h[j][4 * q + 2], h[j][4 * q + 3]);
+      y = fmaf(Dd, xv[j], y);
+      g[o] = from_f32<bf16>(y * silu(zv[j]));
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) st[q] = make_float4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
-    y = fmaf(Dd, xv, y);
-    g[o] = from_f32<bf16>(y * silu(zv));
   }
 }
 
@@ -399,9 +448,16 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
                              const float* A_log, const float* D, float* ssm_state,
                              const int32_t* rows, bf16* g, int M, int d_inner, int dt_rank,
                              hipStream_t s) {
-  hipLaunchKernelGGL(dec_update_kernel, dim3(d_inner / UPD_CH, (M + UPD_MT - 1) / UPD_MT),
-                     dim3(256), 0, s, xh, z, delta, Bm,
-                     Cm, W_dt, b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
+  const dim3 grid(d_inner / UPD_CH, (M + UPD_MT - 1) / UPD_MT);
+  if (dt_rank == 256)
+    hipLaunchKernelGGL(dec_update_kernel<64>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
+                       b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
+  else if (dt_rank == 128)
+    hipLaunchKernelGGL(dec_update_kernel<32>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
+                       b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
+  else
+    hipLaunchKernelGGL(dec_update_kernel<0>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
+                       b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
   return hipGetLastError();
 }
 

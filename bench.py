@@ -52,7 +52,9 @@ def kernel_work(T: int, dm: int, di: int, R: int, N: int = 16):
 
 
 def bound_of(name: str) -> str:
-    return "mfma" if name in ("in_proj", "out_proj") else "hbm"
+    if name in ("in_proj", "out_proj"):
+        return "mfma"
+    return "alu" if name in SCAN_SLOTS else "hbm"
 
 
 def recorded_traffic(kernel: str):
@@ -202,6 +204,8 @@ def main():
             k["alu_frac"] = round(updates * SCAN_SLOTS[name] / VALU_LANE_OPS / (avg * 1e-3), 4)
         if b == "mfma":
             k["frac"] = round(k["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+        elif b == "alu":
+            k["frac"] = k["alu_frac"]
         elif k["gbs"] is not None:
             k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
         kernels[name] = k
@@ -216,6 +220,10 @@ def main():
                     "traffic_note": "HBM-side bytes per launch = 2 x FETCH_SIZE + WRITE_SIZE "
                                     "(calibrated on a 1 GiB copy); algorithmic bytes "
                                     f"{kernel_work(T, d.d_model, d.d_inner, d.dt_rank)[dom][1]:.4g}"}
+        elif kd["bound"] == "alu":
+            roof = {"kernel": dom, "bound": "alu", "achieved": kd["alu_frac"] * VALU_LANE_OPS / 1e12,
+                    "peak": VALU_LANE_OPS / 1e12, "unit": "T VALU lane-slots/s",
+                    "frac": kd["alu_frac"], "traffic": None}
         else:
             roof = {"kernel": dom, "bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": kd["frac"], "traffic": None}

@@ -153,9 +153,11 @@ void plan_chunks(const jm_layer_dims& d, int64_t T, int32_t* chunk_len, int32_t*
   if (g_chunk_override > 0) {
     cl = g_chunk_override;
   } else {
-    // Aim for ~2048 workgroups (8 per CU) across channel groups x chunks.
+    // Aim for ~16384 workgroups across channel groups x chunks: 8 are resident per CU at a
+    // time, and many short chunks (256 tokens for one 128K sequence at d_inner 8192) keep
+    // every CU busy to the end; fewer, longer chunks leave the last round partly idle.
     const int64_t groups = d.d_inner / scan_block(d.d_inner);
-    const int64_t want = (2048 + groups - 1) / groups;
+    const int64_t want = (16384 + groups - 1) / groups;
     cl = (T + want - 1) / want;
     if (cl < 64) cl = 64;
     cl = (cl + 15) / 16 * 16;

@@ -15,12 +15,67 @@
 //                    the final state of every sequence that ends in it.
 // Sequence starts inside a chunk reset the state to the sequence's initial state
 // (or zero); exp is evaluated as exp2 with A pre-scaled by log2(e).
+//
+// Phases A and C are bound by VALU issue (per state and token: two multiplies, one FMA,
+// one exp2; phase C adds the C_t.h FMA). Both run at 8 waves per SIMD (at most 64 VGPRs),
+// which the in-place update h = dx*B + h*exp2(dt*A) allows (the form fma(e, h, dx*B) makes
+// the compiler alternate registers and copy them back every token). Per-token rows are
+// reached through buffer instructions from a wave-uniform row base with 32-bit lane offsets,
+// so all per-token address arithmetic is scalar, and each token's lane inputs are loaded
+// while the previous token is computed.
 #include "jm_internal.h"
 
 namespace jm {
 namespace {
 
 constexpr int NS = 16;   // d_state
+
+// Buffer-resource loads and stores: a wave-uniform base (scalar registers) plus a 32-bit
+// per-lane byte offset, so per-token addressing stays in scalar arithmetic.
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+#endif
+__device__ __forceinline__ float ld_f32(const void* base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc_of(base), (int)off, 0, 0));
+#else
+  return 0.0f;
+#endif
+}
+// An activation's bits, kept as a 32-bit value until it is used (two 16-bit loads in flight
+// would otherwise be packed into one register, which waits for both).
+template <typename T> __device__ __forceinline__ uint32_t ld_bits(const void* base, uint32_t off);
+template <> __device__ __forceinline__ uint32_t ld_bits<float>(const void* base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_amdgcn_raw_buffer_load_b32(rsrc_of(base), (int)off, 0, 0);
+#else
+  return 0u;
+#endif
+}
+template <> __device__ __forceinline__ uint32_t ld_bits<bf16>(const void* base, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rsrc_of(base), (int)off, 0, 0);
+#else
+  return 0u;
+#endif
+}
+template <typename T> __device__ __forceinline__ float bits_f32(uint32_t v);
+template <> __device__ __forceinline__ float bits_f32<float>(uint32_t v) { return __uint_as_float(v); }
+template <> __device__ __forceinline__ float bits_f32<bf16>(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ void st_act(void* base, uint32_t off, float v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc_of(base), (int)off, 0, 0);
+#endif
+}
+__device__ __forceinline__ void st_act(void* base, uint32_t off, bf16 v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rsrc_of(base),
+                                        (int)off, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n_seqs, int64_t t) {
   int lo = 0, hi = n_seqs - 1;
@@ -53,7 +108,7 @@ __device__ __forceinline__ void store16(float* __restrict__ p, const float v[NS]
 // ROWS: whether initial states go through a slot map (init_rows); a compile-time choice so
 // the plain path keeps its register allocation and schedule.
 template <typename T, bool ROWS>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                              const float* __restrict__ A_log, const float* __restrict__ Bm,
                              const float* __restrict__ init,
@@ -71,6 +126,15 @@ void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ 
   for (int n = 0; n < NS; ++n) h[n] = 0.0f;
   float dsum = 0.0f;
   bool reset = false;
+  // Per-token rows are addressed as a wave-uniform row pointer (advanced with scalar
+  // arithmetic) plus this lane's 32-bit byte offset; the next token's dt and x are in
+  // flight while the current one is computed (the last token re-reads itself).
+  const uint32_t of = (uint32_t)d * 4u, oa = (uint32_t)d * (uint32_t)sizeof(T);
+  const float* dtp = dt + t0 * d_inner;
+  const T* xp = x + t0 * d_inner;
+  const float* bp = Bm + t0 * NS;
+  float pdt = ld_f32(dtp, of);
+  uint32_t px = ld_bits<T>(xp, oa);
   int i = find_seq(cu, n_seqs, t0);
   int64_t t = t0;
   while (t < t1) {
@@ -85,27 +149,24 @@ void scan_chunk_state_kernel(const T* __restrict__ x, const float* __restrict__ 
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
     }
     const int64_t e = s_end < t1 ? s_end : t1;
-    // Two tokens per iteration with alternating state registers (no copies).
-    auto step = [&](int64_t tc, const float (&hin)[NS], float (&hout)[NS]) {
-      const float dtv = dt[tc * d_inner + d];
-      const float dx = dtv * to_f32(x[tc * d_inner + d]);
-      const float* b = Bm + tc * NS;
+    const int cnt = (int)(e - t);
+    const int last = (int)(t1 - 1 - t);     // tokens left in the chunk after this one
+    for (int j = 0; j < cnt; ++j) {
+      const float dtv = pdt;
+      const float xv = bits_f32<T>(px);
+      const int64_t step = j < last ? d_inner : 0;
+      dtp += step;
+      xp += step;
+      pdt = ld_f32(dtp, of);
+      px = ld_bits<T>(xp, oa);
+      const float dx = dtv * xv;
 #pragma unroll
       for (int n = 0; n < NS; ++n)
-        hout[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), hin[n], dx * b[n]);
+        h[n] = fmaf(dx, bp[n], h[n] * __builtin_amdgcn_exp2f(dtv * a2[n]));
+      bp += NS;
       dsum += dtv;
-    };
-    float h2[NS];
-    for (; t + 1 < e; t += 2) {
-      step(t, h, h2);
-      step(t + 1, h2, h);
     }
-    if (t < e) {
-      step(t, h, h2);
-#pragma unroll
-      for (int n = 0; n < NS; ++n) h[n] = h2[n];
-      ++t;
-    }
+    t = e;
     ++i;
   }
   float P[NS];
@@ -148,7 +209,7 @@ void scan_chunk_carry_kernel(const float* __restrict__ agg_P, const float* __res
 }
 
 template <typename T, bool ROWS>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__ dt,
                               const float* __restrict__ A_log, const float* __restrict__ Bm,
                               const float* __restrict__ Cm, const float* __restrict__ Dv,
@@ -169,6 +230,18 @@ void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__
   else
 #pragma unroll
     for (int n = 0; n < NS; ++n) h[n] = 0.0f;
+  // Per-token rows are addressed as a wave-uniform row pointer (advanced with scalar
+  // arithmetic) plus this lane's 32-bit byte offset; the next token's inputs are in
+  // flight while the current one is computed (the last token re-reads itself).
+  const uint32_t of = (uint32_t)d * 4u, oa = (uint32_t)d * (uint32_t)sizeof(T);
+  const char* dtp = (const char*)(dt + t0 * d_inner);
+  const char* xp = (const char*)(x + t0 * d_inner);
+  const char* zp = (const char*)(z + t0 * d_inner);
+  char* gp = (char*)(g + t0 * d_inner);
+  const float* bp = Bm + t0 * NS;
+  const float* cp = Cm + t0 * NS;
+  float pdt = ld_f32(dtp, of);
+  uint32_t px = ld_bits<T>(xp, oa), pz = ld_bits<T>(zp, oa);
   int i = find_seq(cu, n_seqs, t0);
   int64_t t = t0;
   while (t < t1) {
@@ -181,35 +254,33 @@ void scan_chunk_output_kernel(const T* __restrict__ x, const float* __restrict__
         for (int n = 0; n < NS; ++n) h[n] = 0.0f;
     }
     const int64_t e = s_end < t1 ? s_end : t1;
-    // Two tokens per iteration: the state alternates between h and h2, so the
-    // loop-carried registers need no copies.
-    auto step = [&](int64_t tc, const float (&hin)[NS], float (&hout)[NS]) {
-      const int64_t o = tc * d_inner + d;
-      const float dtv = dt[o];
-      const float xv = to_f32(x[o]);
-      const float zv = to_f32(z[o]);
+    const int cnt = (int)(e - t);
+    const int last = (int)(t1 - 1 - t);
+    for (int j = 0; j < cnt; ++j) {
+      const float dtv = pdt;
+      const float xv = bits_f32<T>(px);
+      const float zv = bits_f32<T>(pz);
+      const int64_t step = j < last ? (int64_t)d_inner : 0;
+      dtp += step * 4;
+      xp += step * (int64_t)sizeof(T);
+      zp += step * (int64_t)sizeof(T);
+      pdt = ld_f32(dtp, of);
+      px = ld_bits<T>(xp, oa);
+      pz = ld_bits<T>(zp, oa);
       const float dx = dtv * xv;
-      const float* b = Bm + tc * NS;
-      const float* c = Cm + tc * NS;
       float y = Dd * xv;
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
-        hout[n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), hin[n], dx * b[n]);
-        y = fmaf(c[n], hout[n], y);
+        // decay the state in place, then add the input term (no register copies)
+        h[n] = fmaf(dx, bp[n], h[n] * __builtin_amdgcn_exp2f(dtv * a2[n]));
+        y = fmaf(cp[n], h[n], y);
       }
-      g[o] = from_f32<T>(y * silu(zv));
-    };
-    float h2[NS];
-    for (; t + 1 < e; t += 2) {
-      step(t, h, h2);
-      step(t + 1, h2, h);
+      st_act(gp, oa, from_f32<T>(y * silu(zv)));
+      gp += (int64_t)d_inner * (int64_t)sizeof(T);
+      bp += NS;
+      cp += NS;
     }
-    if (t < e) {
-      step(t, h, h2);
-#pragma unroll
-      for (int n = 0; n < NS; ++n) h[n] = h2[n];
-      ++t;
-    }
+    t = e;
     if (e == s_end && final_state) store16(final_state + ((int64_t)i * d_inner + d) * NS, h);
     ++i;
   }

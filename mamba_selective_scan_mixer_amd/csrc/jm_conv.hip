@@ -42,6 +42,31 @@ __device__ __forceinline__ void store8(T* p, const float v[VEC]) {
   }
 }
 
+// 8 channels of one token as loaded (bit patterns), converted only where they are used, so a
+// load in flight is not waited for when it is moved between registers.
+template <typename T> struct RawRow;
+template <> struct RawRow<bf16> { uint4 a; };
+template <> struct RawRow<float> { uint4 a, b; };
+__device__ __forceinline__ RawRow<bf16> load_raw(const bf16* p) {
+  return RawRow<bf16>{*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ RawRow<float> load_raw(const float* p) {
+  return RawRow<float>{reinterpret_cast<const uint4*>(p)[0], reinterpret_cast<const uint4*>(p)[1]};
+}
+__device__ __forceinline__ void unpack_raw(const RawRow<bf16>& r, float v[VEC]) {
+  const uint32_t u[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(u[j] << 16);
+    v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack_raw(const RawRow<float>& r, float v[VEC]) {
+  const uint32_t u[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __uint_as_float(u[j]);
+}
+
 // Largest i in [0, n_seqs) with cu[i] <= t.
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int n_seqs, int64_t t) {
   int lo = 0, hi = n_seqs - 1;
@@ -103,32 +128,51 @@ void conv_silu_kernel(const T* __restrict__ x, T* __restrict__ xh,
       for (int j = 0; j < VEC; ++j) win[q][j] = hist(init, init_rows, i, d_inner, d0 + j, back);
     }
   }
-  for (int64_t t = t0; t < t1; ++t) {
-    if (t == s_end) {   // next sequence starts here: restart the window from its history
-      ++i;
-      s_begin = t;
-      s_end = cu[i + 1];
+  // Tokens in groups of PF: the next group's rows are loaded (kept raw) while the current
+  // group is computed; the loads past the run's end re-read its last row.
+  constexpr int PF = 4;
+  RawRow<T> cur[PF], nxt[PF];
+  const int64_t tl = t1 - 1;
 #pragma unroll
-      for (int q = 0; q < KC - 1; ++q)
+  for (int q = 0; q < PF; ++q) cur[q] = load_raw(x + (t0 + q < tl ? t0 + q : tl) * d_inner + d0);
+  for (int64_t t = t0; t < t1; t += PF) {
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-          win[q][j] = hist(init, init_rows, i, d_inner, d0 + j, KC - 1 - q);
+    for (int q = 0; q < PF; ++q) {
+      const int64_t p = t + PF + q;
+      nxt[q] = load_raw(x + (p < tl ? p : tl) * d_inner + d0);
     }
-    float cur[VEC], out[VEC];
-    load8(x + t * d_inner + d0, cur);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      float c = b[j];
-      c = fmaf(w[j][0], win[0][j], c);
-      c = fmaf(w[j][1], win[1][j], c);
-      c = fmaf(w[j][2], win[2][j], c);
-      c = fmaf(w[j][3], cur[j], c);
-      out[j] = silu(c);
-      win[0][j] = win[1][j];
-      win[1][j] = win[2][j];
-      win[2][j] = cur[j];
+    for (int q = 0; q < PF; ++q) {
+      const int64_t tq = t + q;
+      if (tq >= t1) break;
+      if (tq == s_end) {   // next sequence starts here: restart the window from its history
+        ++i;
+        s_begin = tq;
+        s_end = cu[i + 1];
+#pragma unroll
+        for (int w2 = 0; w2 < KC - 1; ++w2)
+#pragma unroll
+          for (int j = 0; j < VEC; ++j)
+            win[w2][j] = hist(init, init_rows, i, d_inner, d0 + j, KC - 1 - w2);
+      }
+      float xc[VEC], out[VEC];
+      unpack_raw(cur[q], xc);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        float c = b[j];
+        c = fmaf(w[j][0], win[0][j], c);
+        c = fmaf(w[j][1], win[1][j], c);
+        c = fmaf(w[j][2], win[2][j], c);
+        c = fmaf(w[j][3], xc[j], c);
+        out[j] = silu(c);
+        win[0][j] = win[1][j];
+        win[1][j] = win[2][j];
+        win[2][j] = xc[j];
+      }
+      store8(xh + tq * d_inner + d0, out);
     }
-    store8(xh + t * d_inner + d0, out);
+#pragma unroll
+    for (int q = 0; q < PF; ++q) cur[q] = nxt[q];
   }
 }
 

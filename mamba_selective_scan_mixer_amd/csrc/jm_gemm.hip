@@ -7,23 +7,26 @@
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation); the fp32 path (small fp32
 // layers) is a plain LDS-tiled FMA kernel.
 //
-// Main bf16 kernel (K % 32 == 0):
+// Main bf16 kernel (K % 64 == 0):
 //   * 256 x 256 macro tile, 512 threads = 8 waves (two per SIMD, so one wave's
 //     waits and address arithmetic overlap the other's MFMAs), wave tile 64 x 128;
 //   * operands go global -> LDS directly (buffer_load_dwordx4 ... lds, no VGPR
-//     staging) through a 4-stage ring of 32-deep K slices, so loads run ~2.5
-//     stages ahead of the matrix cores; waits are explicit vmcnt counts;
-//   * LDS rows are 32 bf16 = 4 chunks of 16 bytes; chunk c of row r sits at
-//     c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)), which keeps the 16-byte fragment
-//     reads of 16 consecutive rows on distinct banks (measured: no conflicts);
-//   * the barrier of each stage sits before its last k16 step: the next stage's
-//     first fragments load while the current MFMAs run, and the instruction order
-//     is pinned with sched_group_barrier;
+//     staging) in 64-deep K slices (128-byte row segments) through two 64 KB
+//     buffers; each half of a slice's load is issued as soon as its buffer is free,
+//     and the waits are explicit vmcnt counts;
+//   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; chunk c of row r sits at
+//     c ^ ((r & 7) ^ ((r >> 3) & 1)), which keeps the 16-byte fragment reads of 16
+//     consecutive rows on distinct banks (measured: no conflicts);
+//   * the barrier of each slice sits in the middle of its last k16 step: the next
+//     slice's first fragments load while the current MFMAs run, and the instruction
+//     order is pinned with sched_group_barrier;
 //   * the MFMA "A" operand is the weight tile and "B" the activation tile, so a
 //     lane owns 4 consecutive output features of one token (8-byte bf16 stores);
 //   * tile order: groups of 4 row blocks share a weight block, and each of the 8
 //     XCDs (workgroups are dealt to them round-robin) gets a contiguous range.
-// Fallback (K % 32 != 0): 128 x 128 tiles staged through registers with zero-
+// x_proj with 288 outputs has its own 256 x 288 kernel (16x16x32 MFMA blocks), and
+// dt_proj + softplus its own store-bound kernel.
+// Fallback (K % 64 != 0): 128 x 128 tiles staged through registers with zero-
 // filled K tails.
 #include "jm_internal.h"
 
@@ -600,6 +603,123 @@ void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16
   }
 }
 
+// ---- x_proj: 256 tokens x 288 outputs (dt_rank 256, then B and C) -------------------------
+// 288 output features are 18 blocks of 16. On the 256 x 256 kernel they would take two column
+// tiles, the second one 7/8 padding; here one workgroup covers all of them. 8 waves as 4
+// (tokens) x 2 (features): wave tile 64 tokens x 144 features in 16x16x32 MFMA blocks (A = a
+// weight block, so a lane's 4 D registers are 4 consecutive features of one token, the shape
+// the epilogue takes). K is staged in 64-deep slices (128-byte rows, swizzled as in the main
+// kernel) through two LDS buffers filled by direct-to-LDS buffer loads.
+constexpr int XP_BM = 256, XP_N = 288, XP_BK = 64;
+constexpr int XP_STAGE = (XP_BM + XP_N) * XP_BK;   // bf16 elements per stage
+constexpr int XP_LDS_BYTES = 2 * XP_STAGE * 2;      // 139,264
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void xproj_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ W,
+                  int64_t ldw, int64_t M, int K, EpiArgs epi) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  bf16* lds = reinterpret_cast<bf16*>(smem);
+  const int64_t m0 = (int64_t)blockIdx.x * XP_BM;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // DMA instructions (1 KB = 8 rows each): X 32 (4 per wave), W 36 (5 for waves 0-3, 4 after)
+  constexpr int XI = 4, WI = 5;
+  const int wi = wave < 4 ? 5 : 4;
+  const int wfirst = wave < 4 ? 5 * wave : 20 + 4 * (wave - 4);
+  uint32_t xoff[XI], woff[WI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int row = (wave * XI + i) * 8 + lane / 8;
+    const int c = (lane % 8) ^ swz64(row);
+    int64_t r = row;
+    if (m0 + r >= M) r = M - 1 - m0;      // past the end: a copy of the last row, never stored
+    xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = (wfirst + i) * 8 + lane / 8;   // < 288 for every instruction issued
+    const int c = (lane % 8) ^ swz64(row);
+    woff[i] = (uint32_t)(((int64_t)row * ldw + c * 8) * 2);
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + m0 * ldx), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)W, (short)0, 0x7fffffff, kBufferRsrcWord3);
+#endif
+  auto issue = [&](int kt, int buf) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    char* base = reinterpret_cast<char*>(lds + buf * XP_STAGE);
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(base + (wave * XI + i) * 1024), 16,
+                                               xoff[i], kt * XP_BK * 2, 0, 0);
+    char* wb = base + XP_BM * XP_BK * 2;
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+      if (i < wi)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(wb + (wfirst + i) * 1024), 16,
+                                                 woff[i], kt * XP_BK * 2, 0, 0);
+#endif
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, kg = lane >> 4;
+  const int sw = swz64(lr);            // every fragment row of this lane is lr mod 16
+  const int offW = XP_BM * XP_BK + (wn * 144 + lr) * XP_BK;
+  const int offX = (wm * 64 + lr) * XP_BK;
+  f32x4 acc[9][4];
+#pragma unroll
+  for (int a = 0; a < 9; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int nk = K / XP_BK;
+  issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // the other buffer was released by the barrier that ended the previous slice
+    if (kt + 1 < nk) {
+      issue(kt + 1, buf ^ 1);
+      if (wave < 4) wait_vmcnt<XI + 5>(); else wait_vmcnt<XI + 4>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();      // this slice has landed for every wave
+    const bf16* st = lds + buf * XP_STAGE;
+#pragma unroll
+    for (int s = 0; s < XP_BK / 32; ++s) {
+      const int c = ((4 * s + kg) ^ sw) << 3;
+      bf16x8 fw[9], fx[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        fx[b] = *reinterpret_cast<const bf16x8*>(&st[offX + b * 16 * XP_BK + c]);
+#pragma unroll
+      for (int a = 0; a < 9; ++a)
+        fw[a] = *reinterpret_cast<const bf16x8*>(&st[offW + a * 16 * XP_BK + c]);
+#pragma unroll
+      for (int a = 0; a < 9; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[a], fx[b], acc[a][b], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_barrier();      // every wave is done with this buffer
+  }
+
+  // D block (16 features x 16 tokens): lane holds token lr, features 4 kg .. 4 kg + 3.
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t m = m0 + wm * 64 + b * 16 + lr;
+    if (m >= M) continue;
+#pragma unroll
+    for (int a = 0; a < 9; ++a) {
+      const int n = wn * 144 + a * 16 + 4 * kg;
+      float v[4] = {acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]};
+      epilogue<bf16, EPI_XPROJ>(epi, m, n, XP_N, v);
+    }
+  }
+}
+
 template <int EPI>
 hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ldw, int64_t M,
                            int N, int K, const EpiArgs& epi, hipStream_t s) {
@@ -612,6 +732,22 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
     else
       hipLaunchKernelGGL(dt_proj_softplus_kernel<8>, grid, dim3(256), 0, s, X, ldx, W, ldw, M, N,
                          epi.bias, epi.outf0);
+    return hipGetLastError();
+  }
+  if (EPI == EPI_XPROJ && N == XP_N && K % XP_BK == 0 &&
+      ((int64_t)XP_BM * ldx + K) * 2 < ((int64_t)1 << 31) &&
+      ((int64_t)XP_N * ldw + K) * 2 < ((int64_t)1 << 31)) {
+    const int64_t n_wg = (M + XP_BM - 1) / XP_BM;
+    if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
+    static bool xp_attr_set = false;   // dynamic LDS above 64 KB must be enabled once
+    if (!xp_attr_set) {
+      hipError_t e = hipFuncSetAttribute((const void*)xproj_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, XP_LDS_BYTES);
+      if (e != hipSuccess) return e;
+      xp_attr_set = true;
+    }
+    hipLaunchKernelGGL(xproj_kernel, dim3((unsigned)n_wg), dim3(512), XP_LDS_BYTES, s, X, ldx, W,
+                       ldw, M, K, epi);
     return hipGetLastError();
   }
   // buffer-load offsets (256 rows + K, in bytes) must fit 31 bits

@@ -5,6 +5,7 @@ branch-free steady loop and the peeled last two stages take different paths depe
 the slice count K / 64. The Jamba widths give 64 and 128 slices and the small test widths
 1 and 2; these cases add 3, 4, 5 and 7 slices (layer widths d_model 192 / 448 and d_inner
 320 / 256), with a token count that leaves a ragged last 256-row tile (300 = 256 + 44).
+The dt_rank 256 case sends x_proj (288 outputs) to its dedicated 256 x 288 kernel.
 
 Each projection is fed exactly the oracle's upstream tensor rounded to bf16 and compared
 with the oracle's projection of that same tensor: the only difference left is the kernel's
@@ -30,6 +31,8 @@ DIMS = {
     # in_proj K = d_model, x_proj / out_proj K = d_inner: slices K / 64
     "k3_k5": synth.LayerDims(d_model=192, d_inner=320, d_state=16, d_conv=4, dt_rank=16),
     "k7_k4": synth.LayerDims(d_model=448, d_inner=256, d_state=16, d_conv=4, dt_rank=16),
+    # dt_rank 256: x_proj has 288 outputs and runs on its own 256 x 288 kernel (5 slices)
+    "xp288_k5": synth.LayerDims(d_model=192, d_inner=320, d_state=16, d_conv=4, dt_rank=256),
 }
 
 

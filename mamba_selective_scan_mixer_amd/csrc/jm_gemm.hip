@@ -519,19 +519,22 @@ void gemm_f32_kernel(const float* __restrict__ X, int64_t ldx,
 // Delta[t, d] = softplus(sum_k delta[t, k] * W[d, k] + b[d]) for dt_rank K = 128 or 256.
 // The fp32 output (8x the bytes of the input row) makes this a store- and VALU-bound
 // kernel, so it is shaped for the stores rather than for the MFMAs:
-//   * a workgroup = 4 waves = 128 channels; wave w keeps the weight rows of channels
+//   * a workgroup = 16 waves = 512 channels; wave w keeps the weight rows of channels
 //     32w..32w+31 in registers for its whole life (MFMA B operand: lane -> channel
-//     lane % 32, k half lane / 32);
+//     lane % 32, k half lane / 32). Every workgroup reads every token row once, so wide
+//     workgroups cut the L2 traffic of the shared token rows (16 channel groups at
+//     d_inner 8192 instead of 64);
 //   * it walks 32-token blocks blockIdx.y, += gridDim.y; each block of token rows is
 //     copied once into LDS (direct-to-LDS loads, double-buffered, issued a block ahead)
 //     and read from there by all four waves as the MFMA A operand. LDS row r holds its
 //     16-byte chunk c at c ^ (r % 16), so the fragment reads of 16 rows hit distinct banks;
 //   * a lane's results are channel lane % 32 of tokens 8(r/4) + 4(lane/32) + r%4, so each
 //     store instruction writes two full 128-byte row segments;
-//   * three workgroups per CU, whose stores overlap each other's loads and math.
-constexpr int DT_CH = 128;
+//   * 4 waves per SIMD, whose stores overlap each other's loads and math.
+constexpr int DT_NW = 16;
+constexpr int DT_CH = 32 * DT_NW;
 template <int KS>   // K / 16
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(64 * DT_NW)
 void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ W,
                              int64_t ldw, int64_t M, int N, const float* __restrict__ bias,
                              float* __restrict__ out) {
@@ -539,7 +542,8 @@ void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16
   constexpr int ROWB = K * 2;                 // bytes per token row
   constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
   constexpr int BLKB = 32 * ROWB;             // bytes per 32-token block
-  constexpr int DPW = BLKB / 1024 / 4;        // 1 KB DMA instructions per wave per block
+  constexpr int NDMA = BLKB / 1024;           // 1 KB DMA instructions per block
+  constexpr int DPW = (NDMA + DT_NW - 1) / DT_NW;   // per wave (some idle when NDMA < DT_NW)
   __shared__ __attribute__((aligned(1024))) char sx[2][BLKB];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -555,12 +559,13 @@ void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16
   // prefetch and the previous block's stores.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   const int64_t nblk = (M + 31) >> 5;
-  // DMA slot of this lane: instruction j of wave w fills LDS bytes [1 KB * (4j + w), +1 KB),
-  // i.e. rows (1024 / ROWB) * (4j + w) + lane / CPR, physical chunk lane % CPR.
+  // DMA slot of this lane: instruction j of wave w fills LDS bytes [1 KB * s, +1 KB) with
+  // s = DT_NW j + w, i.e. rows (1024 / ROWB) s + lane / CPR, physical chunk lane % CPR.
   auto issue = [&](int64_t blk, int buf) {
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
-      const int slot = 4 * j + wave;
+      const int slot = DT_NW * j + wave;
+      if (slot >= NDMA) break;
       const int r = slot * (1024 / ROWB) + lane / CPR;
       const int c = (lane % CPR) ^ (r & 15);
       int64_t t = (blk << 5) + r;
@@ -727,10 +732,10 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
     const int64_t nblk = (M + 31) / 32;
     const dim3 grid(N / DT_CH, (unsigned)(nblk < 32 ? nblk : 32));
     if (K == 256)
-      hipLaunchKernelGGL(dt_proj_softplus_kernel<16>, grid, dim3(256), 0, s, X, ldx, W, ldw, M, N,
+      hipLaunchKernelGGL(dt_proj_softplus_kernel<16>, grid, dim3(64 * DT_NW), 0, s, X, ldx, W, ldw, M, N,
                          epi.bias, epi.outf0);
     else
-      hipLaunchKernelGGL(dt_proj_softplus_kernel<8>, grid, dim3(256), 0, s, X, ldx, W, ldw, M, N,
+      hipLaunchKernelGGL(dt_proj_softplus_kernel<8>, grid, dim3(64 * DT_NW), 0, s, X, ldx, W, ldw, M, N,
                          epi.bias, epi.outf0);
     return hipGetLastError();
   }

@@ -32,15 +32,14 @@ __device__ __forceinline__ float fast_exp(float v) { return __builtin_amdgcn_exp
 __device__ __forceinline__ float silu(float v) {
   return v * __builtin_amdgcn_rcpf(1.0f + fast_exp(-v));
 }
-// log1p(x) for x in [0, 1] with hardware log2: Kahan's identity
-// log1p(x) = x * ln(u) / (u - 1), u = fl(1 + x), which cancels the rounding of
-// 1 + x and keeps a few-ulp relative error even when x is tiny (u == 1 -> x).
-// The quotient uses the hardware reciprocal (about 1 ulp) instead of an IEEE divide.
+// log1p(x) for x in [0, 1] with hardware log2. u = fl(1 + x) carries a rounding error
+// e = x - (u - 1), computed exactly (Sterbenz), and ln(1 + x) = ln(u) + e / u + O(e^2).
+// With e / u taken as e the dropped part is e (1/u - 1), at most 2^-24 x for small x and
+// 2^-25 near x = 1: a relative error of order 2^-24 everywhere, so tiny x keeps full
+// relative precision (u == 1 gives exactly x) without a division or reciprocal.
 __device__ __forceinline__ float log1p_unit(float x) {
   const float u = 1.0f + x;
-  const float d = u - 1.0f;
-  const float l = __builtin_amdgcn_logf(u) * 0.69314718055994531f;
-  return d == 0.0f ? x : x * l * __builtin_amdgcn_rcpf(d);
+  return fmaf(__builtin_amdgcn_logf(u), 0.69314718055994531f, x - (u - 1.0f));
 }
 // softplus(v) = ln(1 + e^v) = max(v, 0) + log1p(e^-|v|): no overflow, and full
 // relative precision for the small step sizes the layer uses (v << 0).

@@ -34,9 +34,12 @@ F32_PROJ = 1e-5
 F32_SCAN = 5e-5
 
 CASES = {
-    # name: (workload, lengths)
-    "tiny_fp32": ("tiny_fp32", [37, 64, 3, 100]),
-    "jamba_bf16": ("prefill_4k", [150, 3, 203]),
+    # name: (workload, lengths, layer sizes (None: the workload's own))
+    "tiny_fp32": ("tiny_fp32", [37, 64, 3, 100], None),
+    "jamba_bf16": ("prefill_4k", [150, 3, 203], None),
+    # dt_rank 128: the dt_proj kernel's 8-slice form (half its waves load no token rows)
+    "rank128_bf16": ("prefill_4k", [150, 3, 203],
+                     synth.LayerDims(d_model=512, d_inner=1024, d_state=16, d_conv=4, dt_rank=128)),
 }
 
 
@@ -54,8 +57,8 @@ def _out_tol(dtype, kind):
 
 @pytest.fixture(params=list(CASES))
 def case(request):
-    name, lengths = CASES[request.param]
-    wl = synth.make_workload(name, lengths=lengths)
+    name, lengths, dims = CASES[request.param]
+    wl = synth.make_workload(name, lengths=lengths, dims=dims)
     rng = np.random.default_rng(7)
     n = len(lengths)
     di = wl.dims.d_inner

@@ -23,7 +23,9 @@
 //   * the MFMA "A" operand is the weight tile and "B" the activation tile, so a
 //     lane owns 4 consecutive output features of one token (8-byte bf16 stores);
 //   * tile order: groups of 4 row blocks share a weight block, and each of the 8
-//     XCDs (workgroups are dealt to them round-robin) gets a contiguous range.
+//     XCDs (workgroups are dealt to them round-robin) gets a contiguous range;
+//   * persistent: one workgroup per CU walks its tiles, issuing the next tile's first
+//     loads before storing the current tile's results.
 // x_proj with 288 outputs has its own 256 x 288 kernel (16x16x32 MFMA blocks), and
 // dt_proj + softplus its own store-bound kernel.
 // Fallback (K % 64 != 0): 128 x 128 tiles staged through registers with zero-
@@ -281,15 +283,18 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   bf16* lds = reinterpret_cast<bf16*>(smem);
 
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, 4, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
+  const int n_tiles = tiles_m * tiles_n;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm0 = (wave / WAVES_N) * TM;
   const int wn0 = (wave % WAVES_N) * TN;
 
+  // Persistent: workgroup b takes tiles b, b + G, b + 2G, ... (G = gridDim.x, a multiple of
+  // 8, so a workgroup stays on one XCD and the tile order per XCD is the one tile_coords
+  // gives). The next tile's first loads are issued before this tile's results are stored, so
+  // their latency hides behind the epilogue.
+  int64_t m0;
+  int n0;
   // Each DMA instruction fills 1 KB of LDS: lane l writes slot l, i.e. row l / CPR,
   // chunk position l % CPR, so it loads the global chunk that belongs there.
   // Rows past M / N are clamped to the last row (their results are never stored).
@@ -297,28 +302,37 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // row, a fixed 32-bit byte offset per lane and instruction, and the k advance in the
   // scalar offset (the host checks that 256 rows + K fit 2^31 bytes).
   uint32_t xoff[XI], woff[WI];
-#pragma unroll
-  for (int i = 0; i < XI; ++i) {
-    const int row = (wave * XI + i) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz64(row);
-    int64_t r = row;
-    if (m0 + r >= M) r = M - 1 - m0;
-    xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < WI; ++i) {
-    const int row = (wave * WI + i) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ swz64(row);
-    int64_t r = row;
-    if (n0 + r >= N) r = N - 1 - n0;
-    woff[i] = (uint32_t)((r * ldw + c * 8) * 2);
-  }
 #if defined(__HIP_DEVICE_COMPILE__)
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(X + m0 * ldx), (short)0, 0x7fffffff, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * ldw), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  __amdgpu_buffer_rsrc_t xr, wr;
 #endif
+  auto setup = [&](int tile) {
+    int tm, tn;
+    tile_coords(tile, n_tiles, tiles_m, tiles_n, 4, tm, tn);
+    m0 = (int64_t)tm * BM;
+    n0 = tn * BN;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int row = (wave * XI + i) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz64(row);
+      int64_t r = row;
+      if (m0 + r >= M) r = M - 1 - m0;
+      xoff[i] = (uint32_t)((r * ldx + c * 8) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int row = (wave * WI + i) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz64(row);
+      int64_t r = row;
+      if (n0 + r >= N) r = N - 1 - n0;
+      woff[i] = (uint32_t)((r * ldw + c * 8) * 2);
+    }
+#if defined(__HIP_DEVICE_COMPILE__)
+    xr = __builtin_amdgcn_make_buffer_rsrc((void*)(X + m0 * ldx), (short)0, 0x7fffffff,
+                                           kBufferRsrcWord3);
+    wr = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * ldw), (short)0, 0x7fffffff,
+                                           kBufferRsrcWord3);
+#endif
+  };
   // the X half and the W half of a stage's DMA, issued at different points of the loop
   auto issue_x = [&](int kt, int buf) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -356,12 +370,6 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   };
 
   f32x16 acc[FN][FM];
-#pragma unroll
-  for (int a = 0; a < FN; ++a)
-#pragma unroll
-    for (int b = 0; b < FM; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
   bf16x8 fw[2][FN], fx[2][FM];
   auto mfma_range = [&](int cur, int lo, int hi) {
 #pragma unroll
@@ -375,101 +383,132 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // buffer; the X half of stage kt+2 goes there at once, the W half during stage kt+1's first
   // k16 step; both are waited for (vmcnt 0) before the barrier that ends stage kt+1.
   const int nk = K / BKC;
+  // stores this wave issues for a whole tile (one per epilogue call)
+  constexpr int NST = FN * FM * 4;
+  int tile = blockIdx.x;
+  setup(tile);
   issue_x(0, 0);
   issue_w(0, 0);
-  if (nk > 1) {
-    issue_x(1, 1);
-    wait_vmcnt<XI>();     // stage 0 complete; stage 1's X half may be in flight
-  } else {
-    wait_vmcnt<0>();
-  }
-  __builtin_amdgcn_s_barrier();
-  load_frags(0, 0, fw[0], fx[0]);
-  int kt = 0;
-  // Steady state (stages kt+1 and kt+2 exist): no conditionals, so the compiler counts
-  // outstanding LDS reads exactly.
-  for (; kt + 2 < nk; ++kt) {
-    const int rb = kt & 1;
+  if (nk > 1) issue_x(1, 1);
+  bool stores_pending = false;   // the previous tile's NST stores were issued after these loads
+  for (;;) {
+    if (nk > 1) {
+      // stage 0 complete; stage 1's X half (and the previous tile's stores) may be in flight
+      if (stores_pending) wait_vmcnt<XI + NST>(); else wait_vmcnt<XI>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int s = 0; s < SPS; ++s) {
-      const int cur = s & 1;
-      if (s == 0) {
-        issue_w(kt + 1, rb ^ 1);
-        load_frags(rb, 1, fw[1], fx[1]);
-        mfma_range(0, 0, NM);
+    for (int a = 0; a < FN; ++a)
 #pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          if (q < WI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
-          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+      for (int b = 0; b < FM; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+    load_frags(0, 0, fw[0], fx[0]);
+    int kt = 0;
+    // Steady state (stages kt+1 and kt+2 exist): no conditionals, so the compiler counts
+    // outstanding LDS reads exactly.
+    for (; kt + 2 < nk; ++kt) {
+      const int rb = kt & 1;
+#pragma unroll
+      for (int s = 0; s < SPS; ++s) {
+        const int cur = s & 1;
+        if (s == 0) {
+          issue_w(kt + 1, rb ^ 1);
+          load_frags(rb, 1, fw[1], fx[1]);
+          mfma_range(0, 0, NM);
+#pragma unroll
+          for (int q = 0; q < NM; ++q) {
+            if (q < WI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
+            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+          }
+        } else if (s + 1 < SPS) {
+          load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
+          mfma_range(cur, 0, NM);
+#pragma unroll
+          for (int q = 0; q < NR; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+        } else {
+          // half the MFMAs, the stage barrier, then the X DMA of stage kt+2 and the next
+          // stage's first fragments under the other half
+          mfma_range(cur, 0, NM / 2);
+          __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
+          wait_vmcnt<0>();
+          __builtin_amdgcn_s_barrier();
+          issue_x(kt + 2, rb);
+          load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
+          mfma_range(cur, NM / 2, NM);
+          constexpr int DPS = (XI + NM / 2 - 1) / (NM / 2);   // DMAs per MFMA slot
+          constexpr int RPS = (NR + NM / 2 - 1) / (NM / 2);   // reads per MFMA slot
+#pragma unroll
+          for (int q = 0; q < NM / 2; ++q) {
+#pragma unroll
+            for (int z = 0; z < DPS; ++z)
+              if (q * DPS + z < XI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+            for (int z = 0; z < RPS; ++z)
+              if (q * RPS + z < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
         }
-      } else if (s + 1 < SPS) {
-        load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
+      }
+    }
+    // Last two stages (nothing more to load after stage kt+1's W half).
+    for (; kt < nk; ++kt) {
+      const int rb = kt & 1;
+#pragma unroll
+      for (int s = 0; s < SPS; ++s) {
+        const int cur = s & 1;
+        if (s == 0 && kt + 1 < nk) issue_w(kt + 1, rb ^ 1);
+        if (s + 1 < SPS) {
+          load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
+        } else if (kt + 1 < nk) {
+          wait_vmcnt<0>();
+          __builtin_amdgcn_s_barrier();
+          load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
+        }
         mfma_range(cur, 0, NM);
-#pragma unroll
-        for (int q = 0; q < NR; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
-      } else {
-        // half the MFMAs, the stage barrier, then the X DMA of stage kt+2 and the next
-        // stage's first fragments under the other half
-        mfma_range(cur, 0, NM / 2);
-        __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        issue_x(kt + 2, rb);
-        load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
-        mfma_range(cur, NM / 2, NM);
-        constexpr int DPS = (XI + NM / 2 - 1) / (NM / 2);   // DMAs per MFMA slot
-        constexpr int RPS = (NR + NM / 2 - 1) / (NM / 2);   // reads per MFMA slot
-#pragma unroll
-        for (int q = 0; q < NM / 2; ++q) {
-#pragma unroll
-          for (int z = 0; z < DPS; ++z)
-            if (q * DPS + z < XI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-#pragma unroll
-          for (int z = 0; z < RPS; ++z)
-            if (q * RPS + z < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        }
       }
     }
-  }
-  // Last two stages (nothing more to load after stage kt+1's W half).
-  for (; kt < nk; ++kt) {
-    const int rb = kt & 1;
-#pragma unroll
-    for (int s = 0; s < SPS; ++s) {
-      const int cur = s & 1;
-      if (s == 0 && kt + 1 < nk) issue_w(kt + 1, rb ^ 1);
-      if (s + 1 < SPS) {
-        load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
-      } else if (kt + 1 < nk) {
-        wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
-      }
-      mfma_range(cur, 0, NM);
-    }
-  }
 
-  // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
-#pragma unroll
-  for (int a = 0; a < FN; ++a)
-#pragma unroll
-    for (int b = 0; b < FM; ++b) {
-      const int64_t m = m0 + wm0 + b * 32 + lrow;
-      if (m >= M) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn0 + a * 32 + 8 * q + 4 * khalf;
-        float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                      acc[a][b][4 * q + 3]};
-        epilogue<bf16, EPI>(epi, m, n, N, v);
-      }
+    // The tile's LDS is no longer read once every wave is here: the next tile's first
+    // loads go out now and land while this tile's results are stored.
+    const int64_t em0 = m0;
+    const int en0 = n0;
+    const int next = tile + (int)gridDim.x;
+    if (next < n_tiles) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's fragment reads done
+      __builtin_amdgcn_s_barrier();
+      setup(next);
+      issue_x(0, 0);
+      issue_w(0, 0);
+      if (nk > 1) issue_x(1, 1);
     }
+    // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
+#pragma unroll
+    for (int a = 0; a < FN; ++a)
+#pragma unroll
+      for (int b = 0; b < FM; ++b) {
+        const int64_t m = em0 + wm0 + b * 32 + lrow;
+        if (m >= M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = en0 + wn0 + a * 32 + 8 * q + 4 * khalf;
+          float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                        acc[a][b][4 * q + 3]};
+          epilogue<bf16, EPI>(epi, m, n, N, v);
+        }
+      }
+    if (next >= n_tiles) break;
+    // a whole tile issued exactly NST stores, all after the loads above
+    stores_pending = em0 + BM <= M && en0 + BN <= N;
+    tile = next;
+  }
 }
 
 // ---- fp32 path ----------------------------------------------------------------------
@@ -771,7 +810,21 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)n_wg), dim3(64 * MS_WM * MS_WN), MS_LDS_BYTES, s, X,
+    // One persistent workgroup per CU (128 KB of LDS each; a multiple of 8 for the XCD
+    // dealing): each tile's first loads are issued before the previous tile's stores, so their
+    // latency hides behind the epilogue (in_proj at 128K tokens: 128 tiles per CU, 2-3% faster
+    // than one workgroup per tile; out_proj, 32 tiles per CU, unchanged).
+    static int n_cu = 0;
+    if (n_cu == 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          n_cu < 8)
+        n_cu = 8;
+    }
+    int64_t grid = n_cu & ~7;
+    if (grid > n_wg) grid = n_wg;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * MS_WM * MS_WN), MS_LDS_BYTES, s, X,
                        ldx, W, ldw, M, N, K, (int)tiles_m, tiles_n, epi);
     return hipGetLastError();
   }

@@ -241,31 +241,66 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
   }
 }
 
-// out = bf16(sum of split-K partials), fixed order.
+// Split-K partial sums of 4 consecutive outputs, added in split order (deterministic). With
+// SPLITS known at compile time every split's load is issued before the first add, so the
+// reduction costs about one memory latency instead of one per split.
+template <int SPLITS>
+__device__ __forceinline__ float4 sum_splits(const float* __restrict__ p, int splits,
+                                             int64_t stride) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if constexpr (SPLITS > 0) {
+    float4 q[SPLITS];
+#pragma unroll
+    for (int s = 0; s < SPLITS; ++s) q[s] = *reinterpret_cast<const float4*>(p + s * stride);
+#pragma unroll
+    for (int s = 0; s < SPLITS; ++s) {
+      v.x += q[s].x; v.y += q[s].y; v.z += q[s].z; v.w += q[s].w;
+    }
+  } else {
+    for (int s = 0; s < splits; ++s) {
+      const float4 q = *reinterpret_cast<const float4*>(p + s * stride);
+      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+    }
+  }
+  return v;
+}
+
+// out = bf16(sum of split-K partials); 4 outputs per thread (count % 4 == 0).
+template <int SPLITS>
 __global__ __launch_bounds__(256)
 void dec_sum_partials_kernel(const float* __restrict__ partial, int splits, int64_t count,
                              bf16* __restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= count) return;
-  float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += partial[s * count + idx];
-  out[idx] = from_f32<bf16>(v);
+  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= count) return;
+  const float4 v = sum_splits<SPLITS>(partial + i4, splits, count);
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 o = {from_f32<bf16>(v.x), from_f32<bf16>(v.y), from_f32<bf16>(v.z),
+                    from_f32<bf16>(v.w)};
+  *reinterpret_cast<bf16x4*>(out + i4) = o;
 }
 
-// Sum split-K partials of x_proj in a fixed order: delta (bf16), B and C (fp32).
+// Sum split-K partials of x_proj: delta (bf16), B and C (fp32); 4 outputs per thread (R and
+// the state width are multiples of 4, so a group never straddles two of them).
+template <int SPLITS>
 __global__ __launch_bounds__(256)
 void dec_xproj_reduce_kernel(const float* __restrict__ partial, int splits, int M, int R,
                              bf16* __restrict__ delta, float* __restrict__ Bm,
                              float* __restrict__ Cm) {
   const int N = R + 2 * NS;
   const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * N) return;
-  const int m = idx / N, n = idx % N;
-  float v = 0.0f;
-  for (int s = 0; s < splits; ++s) v += partial[((int64_t)s * M + m) * N + n];
-  if (n < R) delta[(int64_t)m * R + n] = from_f32<bf16>(v);
-  else if (n < R + NS) Bm[m * NS + (n - R)] = v;
-  else Cm[m * NS + (n - R - NS)] = v;
+  if (idx >= M * (N / 4)) return;
+  const int m = idx / (N / 4), n = (idx % (N / 4)) * 4;
+  const float4 v = sum_splits<SPLITS>(partial + (int64_t)m * N + n, splits, (int64_t)M * N);
+  if (n < R) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 o = {from_f32<bf16>(v.x), from_f32<bf16>(v.y), from_f32<bf16>(v.z),
+                      from_f32<bf16>(v.w)};
+    *reinterpret_cast<bf16x4*>(delta + (int64_t)m * R + n) = o;
+  } else if (n < R + NS) {
+    *reinterpret_cast<float4*>(Bm + m * NS + (n - R)) = v;
+  } else {
+    *reinterpret_cast<float4*>(Cm + m * NS + (n - R - NS)) = v;
+  }
 }
 
 // dt_proj (MFMA) + softplus + state update + D skip + gate for 32 channels x 32 tokens
@@ -438,8 +473,13 @@ hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf
   e.partial = partial;
   hipError_t err = launch_dec_gemm<4, 1, DEC_PARTIAL>(xh, W_x, M, N, d_inner, splits, e, s);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dec_xproj_reduce_kernel, dim3((M * N + 255) / 256), dim3(256), 0, s,
-                     partial, splits, M, dt_rank, delta, Bm, Cm);
+  const dim3 rgrid((M * (N / 4) + 255) / 256);
+  if (splits == 16)   // d_inner 8192
+    hipLaunchKernelGGL(dec_xproj_reduce_kernel<16>, rgrid, dim3(256), 0, s, partial, splits, M,
+                       dt_rank, delta, Bm, Cm);
+  else
+    hipLaunchKernelGGL(dec_xproj_reduce_kernel<0>, rgrid, dim3(256), 0, s, partial, splits, M,
+                       dt_rank, delta, Bm, Cm);
   return hipGetLastError();
 }
 
@@ -469,8 +509,9 @@ hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial,
                                                       OUTPROJ_SPLITS, e, s);
   if (err != hipSuccess) return err;
   const int64_t count = (int64_t)M * d_model;
-  hipLaunchKernelGGL(dec_sum_partials_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
-                     s, partial, OUTPROJ_SPLITS, count, out);
+  hipLaunchKernelGGL(dec_sum_partials_kernel<OUTPROJ_SPLITS>,
+                     dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, s, partial,
+                     OUTPROJ_SPLITS, count, out);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@
 //   3. adjoint into each chunk (bwd_carry_kernel), sequential over chunks in reverse:
 //      I_{K-1} = 0, I_{k-1} = L_k + P_k I_k;
 //   4. main (bwd_main_kernel), per chunk: a forward pass from the entry state keeps the
-//      state before every 8-token sub-block (in registers, as a stack); then, sub-block by
+//      state before every 8-token sub-block (in registers); then, sub-block by
 //      sub-block from the end, the 8 states after each token are recomputed into registers
 //      (with their decays) and the adjoint runs backwards from I_k, emitting per-token
 //      gradients;
@@ -44,6 +44,7 @@ constexpr int BW_CHUNK = 64;         // tokens per chunk
 constexpr int BW_CH = 64;            // channels per workgroup
 constexpr int SUB = 8;               // tokens per sub-block
 constexpr int NSUB = BW_CHUNK / SUB; // sub-blocks per chunk
+static_assert(NSUB * 4 == 32, "a lane's sub-block entry states fill one 32-element vector");
 
 __device__ __forceinline__ int find_seq_b(const int32_t* __restrict__ cu, int n_seqs, int64_t t) {
   int lo = 0, hi = n_seqs - 1;
@@ -72,6 +73,8 @@ __device__ __forceinline__ void zero4(float v[4]) { v[0] = v[1] = v[2] = v[3] = 
 // compiler would otherwise hoist out of the loop and keep live (or spill) for every array.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// the per-sub-block entry states of a lane (4 states x 8 sub-blocks), kept in registers
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 #if defined(__HIP_DEVICE_COMPILE__)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
@@ -534,9 +537,11 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
   const float Dd = Dv[d];
   __syncthreads();
 
-  // pass 1: forward from the entry state; the state entering each sub-block is pushed on a
-  // register stack (ck[NSUB - 1] is the top)
-  float ck[NSUB][4];
+  // pass 1: forward from the entry state; the state entering sub-block sb is kept in
+  // ck[4 sb .. 4 sb + 3]. ck is one register vector indexed by the (wave-uniform) sub-block:
+  // the compiler reaches its elements through GPR indexing, where a shifted stack of
+  // separate registers cost a copy of every entry per sub-block in both passes.
+  f32x32 ck;
   {
     int i = find_seq_b(cu, n_seqs, s);
     float h[4];
@@ -556,11 +561,7 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
         if (h0) ld4_at(h0 + (int64_t)i * dn, lo4, h); else zero4(h);
       }
 #pragma unroll
-      for (int m = 0; m < NSUB - 1; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ck[m][j] = ck[m + 1][j];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ck[NSUB - 1][j] = h[j];
+      for (int j = 0; j < 4; ++j) ck[4 * sb + j] = h[j];
       if (len == SUB && nstart >= t0 + SUB)
         forward_sub<false>(sxd, sbc, r0, len, t0, dl, q, a2, h, i, nstart, cu, h0, dn, lo4);
       else
@@ -586,11 +587,7 @@ void bwd_main_kernel(const T* __restrict__ x, const float* __restrict__ dt,
     if (sb > 0) fetch_zg(z, dg, t0 - SUB, d_inner, lo_el * (uint32_t)sizeof(T), true, nxt);
     float hq[SUB + 1][4], av[SUB][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hq[0][j] = ck[NSUB - 1][j];
-#pragma unroll
-    for (int m = NSUB - 1; m > 0; --m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ck[m][j] = ck[m - 1][j];
+    for (int j = 0; j < 4; ++j) hq[0][j] = ck[4 * sb + j];
     // sequence of the sub-block's last token; a full sub-block inside one sequence takes the
     // path without per-token boundary checks
     int il = iseq;

@@ -75,3 +75,26 @@ def test_layer_at_odd_slice_counts(wl):
              ssm=rel_err(ssm, ref["ssm_state"]))
     print(f"layer d_model {wl.dims.d_model} d_inner {wl.dims.d_inner}: {e}", flush=True)
     assert max(e.values()) < TOL["bf16"], e
+
+
+def test_persistent_tiles_with_a_ragged_row_block():
+    """Jamba widths at 4196 tokens (17 row blocks, the last 100 rows): in_proj has 1088 tiles
+    and out_proj 272, so the persistent workgroups take several tiles each and some follow a
+    partial tile with a whole one (the wait that opens a tile then also covers the previous
+    tile's stores). Both projections against the oracle at the bf16 rounding bound."""
+    wl = synth.make_workload("prefill_4k", lengths=[4196], dtype="bf16")
+    layer = device_layer(wl)
+    w = oracle.as_f64(wl.weights)
+    d = wl.dims
+    x, z = jm.jm_stage_in_proj(layer, to_dev(wl.u, "bf16"))
+    rng = np.random.default_rng(11)
+    g_in = _bf16(rng.standard_normal((4196, d.d_inner)) * 0.05)
+    out = jm.jm_stage_out_proj(layer, to_dev(g_in, "bf16"))
+    torch.cuda.synchronize()
+    xr, zr = oracle.in_proj(wl.u, w["in_proj_w"], d.d_inner)
+    e = dict(x=rel_err(to_np(x), xr), z=rel_err(to_np(z), zr),
+             out=rel_err(to_np(out), oracle.out_proj(g_in, w["out_proj_w"])))
+    # the last (partial) row block on its own as well
+    e["x_tail"] = rel_err(to_np(x)[4096:], xr[4096:])
+    print(f"persistent 4196 tokens: {e}", flush=True)
+    assert max(e.values()) < BF16_OUT, e

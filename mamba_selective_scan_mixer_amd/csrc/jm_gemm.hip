@@ -32,6 +32,8 @@
 // filled K tails.
 #include "jm_internal.h"
 
+#include <atomic>
+
 namespace jm {
 namespace {
 
@@ -764,6 +766,22 @@ void xproj_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restric
   }
 }
 
+// Per-device launch set-up, done once per device and thread-safe: each GPU a process uses
+// gets its own flag (the LDS attribute is set for the current device) and its own CU count.
+constexpr int kMaxDevices = 64;
+hipError_t current_device(int& dev) {
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  return dev >= 0 && dev < kMaxDevices ? hipSuccess : hipErrorInvalidDevice;
+}
+hipError_t allow_big_lds_once(std::atomic<bool> (&done)[kMaxDevices], int dev, const void* fn,
+                              int bytes) {
+  if (done[dev].load(std::memory_order_acquire)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done[dev].store(true, std::memory_order_release);
+  return e;
+}
+
 template <int EPI>
 hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ldw, int64_t M,
                            int N, int K, const EpiArgs& epi, hipStream_t s) {
@@ -783,13 +801,13 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
       ((int64_t)XP_N * ldw + K) * 2 < ((int64_t)1 << 31)) {
     const int64_t n_wg = (M + XP_BM - 1) / XP_BM;
     if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
-    static bool xp_attr_set = false;   // dynamic LDS above 64 KB must be enabled once
-    if (!xp_attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)xproj_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, XP_LDS_BYTES);
-      if (e != hipSuccess) return e;
-      xp_attr_set = true;
-    }
+    // dynamic LDS above 64 KB must be enabled once per device
+    static std::atomic<bool> xp_attr_set[kMaxDevices];
+    int dev = 0;
+    hipError_t e = current_device(dev);
+    if (e == hipSuccess)
+      e = allow_big_lds_once(xp_attr_set, dev, (const void*)xproj_kernel, XP_LDS_BYTES);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(xproj_kernel, dim3((unsigned)n_wg), dim3(512), XP_LDS_BYTES, s, X, ldx, W,
                        ldw, M, K, epi);
     return hipGetLastError();
@@ -803,24 +821,22 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
     const int64_t n_wg = tiles_m * tiles_n;
     if (n_wg > 0x7fffffff) return hipErrorInvalidValue;
     auto kern = gemm_bf16_kernel<MS_BM, MS_BN, MS_WM, MS_WN, MS_BK, EPI>;
-    static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled once
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, MS_LDS_BYTES);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+    static std::atomic<bool> attr_set[kMaxDevices];   // per device, as for x_proj
+    int dev = 0;
+    hipError_t e = current_device(dev);
+    if (e == hipSuccess) e = allow_big_lds_once(attr_set, dev, (const void*)kern, MS_LDS_BYTES);
+    if (e != hipSuccess) return e;
     // One persistent workgroup per CU (128 KB of LDS each; a multiple of 8 for the XCD
     // dealing): each tile's first loads are issued before the previous tile's stores, so their
     // latency hides behind the epilogue (in_proj at 128K tokens: 128 tiles per CU, 2-3% faster
     // than one workgroup per tile; out_proj, 32 tiles per CU, unchanged).
-    static int n_cu = 0;
+    static std::atomic<int> cu_count[kMaxDevices];
+    int n_cu = cu_count[dev].load(std::memory_order_relaxed);
     if (n_cu == 0) {
-      int dev = 0;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
           n_cu < 8)
         n_cu = 8;
+      cu_count[dev].store(n_cu, std::memory_order_relaxed);
     }
     int64_t grid = n_cu & ~7;
     if (grid > n_wg) grid = n_wg;

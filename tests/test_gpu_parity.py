@@ -110,6 +110,42 @@ def test_deterministic(jamba_small):
         assert np.array_equal(x, y)
 
 
+def test_concurrent_calls_on_two_streams(jamba_small):
+    """Two host threads call the prefill at the same time, each on its own stream with its own
+    workspace and input (the boundary allows concurrent calls that share nothing writable);
+    each result equals the same call made alone, bit for bit."""
+    import threading
+    wl = jamba_small[0.0]
+    layer = device_layer(wl)
+    rng = np.random.default_rng(21)
+    us = [wl.u, synth.round_bf16(rng.standard_normal(wl.u.shape))]
+    alone = [gpu_prefill(wl, layer, u=u) for u in us]
+    cu_d = torch.as_tensor(wl.cu_seqlens, dtype=torch.int32).cuda()
+    u_d = [to_dev(u, wl.dtype) for u in us]
+    streams = [torch.cuda.Stream() for _ in us]
+    torch.cuda.synchronize()
+    res, errs = [None] * len(us), []
+
+    def run(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                res[i] = jm.jamba_mamba_prefill(layer, u_d[i], cu_d, wl.cu_seqlens,
+                                                stream=streams[i])
+        except Exception as e:   # reported below, from the main thread
+            errs.append(e)
+
+    threads = [threading.Thread(target=run, args=(i,)) for i in range(len(us))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errs, errs
+    for i in range(len(us)):
+        for x, y in zip(alone[i], res[i]):
+            assert np.array_equal(x, to_np(y)), i
+
+
 def test_sequences_are_isolated_bitwise():
     jm.set_scan_chunk_len(32)
     wl = synth.make_workload("packed_varlen", seed=5, D_value=0.0, n_seqs=4, lengths=[50, 3, 77, 40])

@@ -5,6 +5,7 @@
 #include "jamba_mamba.h"
 #include "jm_internal.h"
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -40,7 +41,7 @@ struct ProfRec {
   const char* name;
   hipEvent_t a, b;
 };
-bool g_prof = false;
+std::atomic<bool> g_prof{false};   // read by every launch, set by jm_profile_enable
 std::mutex g_prof_mu;
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;

@@ -634,17 +634,20 @@ void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sx[buf][t0r * ROWB + c * 16]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w[s], acc, 0, 0, 0);
     }
+    // Delta is written once and first read back by the scan after all of it is written (4 GiB
+    // at 128K tokens, far more than the caches): streaming (non-temporal) stores.
     const int64_t t0 = blk << 5;
     float* op = out + (t0 + 4 * kh) * N + ch;
     if (t0 + 32 <= M) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        op[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = softplus(acc[r] + b);
+        __builtin_nontemporal_store(softplus(acc[r] + b), &op[(int64_t)(8 * (r >> 2) + (r & 3)) * N]);
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (t0 + 4 * kh + 8 * (r >> 2) + (r & 3) < M)
-          op[(int64_t)(8 * (r >> 2) + (r & 3)) * N] = softplus(acc[r] + b);
+          __builtin_nontemporal_store(softplus(acc[r] + b),
+                                      &op[(int64_t)(8 * (r >> 2) + (r & 3)) * N]);
     }
   }
 }

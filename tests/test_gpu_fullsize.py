@@ -114,6 +114,40 @@ def test_prefill_128k_constructed_input(D_value):
     assert max(e.values()) < TOL["bf16"], e
 
 
+def test_prefill_past_32bit_offsets():
+    """One sequence of 2^19 + 300 tokens: every activation buffer passes 2^32 bytes (x, z,
+    x_hat and g are 8.6 GB each, Delta 17 GB) and token x channel indexes pass 2^31, so a
+    32-bit byte offset or element index anywhere on the path would show. The input is built
+    as in the 128K constructed case: random head and tail of 512 tokens around zeros, checked
+    against the oracle at both ends and for exact zeros between."""
+    P = 512
+    base = synth.make_workload("prefill_4k", D_value=1.0, lengths=[2 * P])
+    T = (1 << 19) + 300
+    layer = device_layer(base)
+    u = torch.zeros((T, base.dims.d_model), dtype=torch.bfloat16, device="cuda")
+    u[:P] = to_dev(base.u[:P], "bf16")
+    u[T - P:] = to_dev(base.u[P:], "bf16")
+    cu_d = torch.as_tensor(np.asarray([0, T], np.int32)).cuda()
+    out, conv, ssm = jm.jamba_mamba_prefill(layer, u, cu_d, [0, T])
+    torch.cuda.synchronize()
+    del u
+    n_nonzero = int(torch.count_nonzero(out[P:T - P]).item())
+    w64 = oracle.as_f64(base.weights)
+    ref_head = oracle.prefill(w64, base.u[:P], [0, P])
+    h_star, a = zero_input_fixed_point(w64)
+    assert np.max(a) ** (T - 2 * P) < 1e-40
+    di = w64["D"].shape[0]
+    ref_tail = oracle.prefill(w64, base.u[P:], [0, P], init_conv=np.zeros((1, di, 3)),
+                              init_ssm=h_star[None])
+    e = dict(head=rel_err(to_np(out[:P]), ref_head["out"]),
+             tail=rel_err(to_np(out[T - P:]), ref_tail["out"]),
+             conv=rel_err(to_np(conv), ref_tail["conv_state"]),
+             ssm=rel_err(to_np(ssm), ref_tail["ssm_state"]))
+    report(f"prefill {T} tokens constructed nonzero_mid={n_nonzero}", **e)
+    assert n_nonzero == 0
+    assert max(e.values()) < TOL["bf16"], e
+
+
 @pytest.mark.parametrize("D_value", [0.0, 1.0])
 def test_decode_b64_full(D_value):
     steps = 1024 if D_value == 0.0 else 64

@@ -111,10 +111,12 @@ __device__ __forceinline__ void st4_at(float* row, uint32_t lo, const float v[4]
   __builtin_amdgcn_raw_buffer_store_b128(r, rsrc_at(row), (int)lo, 0, 0);
 #endif
 }
+// Streaming (non-temporal, cache-policy bit nt) store for the per-token gradient rows: 12 bytes
+// per token and channel that nothing in the backward reads again.
 __device__ __forceinline__ void st2_at(float* row, uint32_t lo, float a, float b) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const u32x2 r = {__float_as_uint(a), __float_as_uint(b)};
-  __builtin_amdgcn_raw_buffer_store_b64(r, rsrc_at(row), (int)lo, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(r, rsrc_at(row), (int)lo, 0, 2);
 #endif
 }
 __device__ __forceinline__ void st1_at(float* row, uint32_t lo, float a) {

@@ -221,8 +221,11 @@ jm_status jm_prefill_plan(const jm_layer_dims *dims, const int32_t *cu_seqlens_h
                           int32_t *n_chunks, jm_chunk_segment *segments,
                           int64_t max_segments, int64_t *n_segments);
 
-/* Chunk length override for the scan (0 = automatic). Process-wide; for tuning
- * and for chunk-count invariance tests. Returns JM_ERR_INVALID_ARG if negative. */
+/* Chunk length override for the scan (0 = automatic). Process-wide, for tuning and
+ * for chunk-count invariance tests: it changes the chunk plan of every later prefill,
+ * plan query and workspace-size query on every thread, so it must not change between a
+ * *_workspace_size query and the call that uses that workspace. Returns
+ * JM_ERR_INVALID_ARG if negative. */
 jm_status jm_set_scan_chunk_len(int32_t chunk_len);
 
 /* ---- Stage entry points (diagnostics) -------------------------------------------
@@ -276,6 +279,26 @@ jm_status jm_stage_scan(const jm_layer_dims *dims, const jm_layer_weights *weigh
 /* out_proj: out = W_out g.  g (T, d_inner) act -> out (T, d_model) act. */
 jm_status jm_stage_out_proj(const jm_layer_dims *dims, const jm_layer_weights *weights,
                             const void *g, int64_t total_tokens, void *out, void *stream);
+
+/* Decode update: the fused step of jamba_mamba_decode_step that follows x_proj (and the
+ * inner norm, which is not applied here), for each of `batch` sequences b:
+ *   Delta_b = softplus(W_dt delta_b + b_dt),  h = exp(Delta_b A) h + Delta_b B_b x_hat_b,
+ *   g_b = (C_b . h + D x_hat_b) * SiLU(z_b),
+ * with the SSM state h updated in place. It runs the kernels the decode step runs.
+ *  x_hat, z    (batch, d_inner) act, read
+ *  delta       (batch, dt_rank) act, read
+ *  B, C        (batch, d_state) fp32, read
+ *  slots       NULL: ssm_state is (batch, d_inner, d_state) fp32 and row b is sequence b's;
+ *              else a device int32 array of `batch` distinct slot ids in [0, n_slots) with an
+ *              equal host copy slots_host (validated), and ssm_state is a cache of n_slots
+ *              rows of which only rows slots[0..batch) are read and written
+ *  g           (batch, d_inner) act, written
+ * batch == 0 is a no-op. Errors as for the other stage entry points. */
+jm_status jm_stage_decode_update(const jm_layer_dims *dims, const jm_layer_weights *weights,
+                                 const void *x_hat, const void *z, const void *delta,
+                                 const float *B, const float *C, int32_t batch,
+                                 const int32_t *slots, const int32_t *slots_host, int32_t n_slots,
+                                 float *ssm_state, void *g, void *stream);
 
 /* ---- Backward of the scan step (training) ----------------------------------------------
  * Gradients of jm_stage_scan's output (g = (scan(x_hat, Delta, A, B, C; h0) + D x_hat) *

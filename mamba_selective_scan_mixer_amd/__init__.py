@@ -14,7 +14,9 @@ sequence in place of a KV cache.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 from typing import Dict, List, Optional, Sequence, Tuple
 
@@ -116,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.jamba_mamba_scan_backward.argtypes = [
             D, W, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
             _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.jm_stage_decode_update.argtypes = [D, W, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                             ctypes.c_int32, _P, _P, _P]
         L.jamba_mamba_decode_step_slots.argtypes = [
             D, W, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
         for name in ("jm_prefill_workspace_size", "jm_decode_workspace_size", "jamba_mamba_prefill",
@@ -123,6 +127,7 @@ def lib() -> ctypes.CDLL:
                      "jm_profile_enable", "jm_profile_reset", "jm_profile_read",
                      "jm_stage_in_proj", "jm_stage_conv", "jm_stage_x_proj", "jm_stage_dt_proj",
                      "jm_stage_scan_workspace_size", "jm_stage_scan", "jm_stage_out_proj",
+                     "jm_stage_decode_update",
                      "jm_prefill_slots_workspace_size", "jamba_mamba_prefill_slots",
                      "jamba_mamba_decode_step_slots", "jm_scan_backward_workspace_size",
                      "jamba_mamba_scan_backward"):
@@ -217,6 +222,19 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _on_call_stream(fn):
+    """Run an entry point with `stream` (when given) as torch's current stream, so that every
+    tensor it allocates (outputs, workspace, device copies of slot ids) belongs to the stream
+    its kernels run on: the caching allocator then reuses that memory only for work ordered
+    after them, and host-to-device copies made here precede the kernels."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        ctx = contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+        with ctx:
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def prefill_workspace_size(dims: LayerDims, n_seqs: int, total_tokens: int) -> int:
     out = ctypes.c_size_t(0)
     _check(lib().jm_prefill_workspace_size(ctypes.byref(dims), n_seqs, total_tokens,
@@ -235,6 +253,7 @@ def _host_cu(cu_seqlens_host) -> Tuple[ctypes.Array, int]:
     return (ctypes.c_int32 * len(vals))(*vals), len(vals) - 1
 
 
+@_on_call_stream
 def jamba_mamba_prefill(layer: MambaLayer, u: torch.Tensor, cu_seqlens: torch.Tensor,
                         cu_seqlens_host: Sequence[int], init_conv_state=None, init_ssm_state=None,
                         out=None, final_conv_state=None, final_ssm_state=None,
@@ -274,6 +293,7 @@ def jamba_mamba_prefill(layer: MambaLayer, u: torch.Tensor, cu_seqlens: torch.Te
     return out, final_conv_state, final_ssm_state
 
 
+@_on_call_stream
 def jamba_mamba_decode_step(layer: MambaLayer, u: torch.Tensor, conv_state: torch.Tensor,
                             ssm_state: torch.Tensor, out=None, workspace=None, stream=None):
     """One token per sequence; updates conv_state and ssm_state in place; returns out."""
@@ -332,6 +352,7 @@ def profile_read() -> Dict[str, Tuple[int, float]]:
 
 # ---- stage entry points (one step of the prefill each; diagnostics) -----------------------
 
+@_on_call_stream
 def jm_stage_in_proj(layer: MambaLayer, u: torch.Tensor, stream=None):
     """[x ; z] = W_in u; returns (x, z), each (T, d_inner)."""
     d, dt = layer.dims, _torch_dtype(layer.dims)
@@ -344,6 +365,7 @@ def jm_stage_in_proj(layer: MambaLayer, u: torch.Tensor, stream=None):
     return x, z
 
 
+@_on_call_stream
 def jm_stage_conv(layer: MambaLayer, x: torch.Tensor, cu_seqlens: torch.Tensor,
                   cu_seqlens_host: Sequence[int], init_conv_state=None,
                   want_final_state: bool = True, stream=None):
@@ -364,6 +386,7 @@ def jm_stage_conv(layer: MambaLayer, x: torch.Tensor, cu_seqlens: torch.Tensor,
     return xh, fc
 
 
+@_on_call_stream
 def jm_stage_x_proj(layer: MambaLayer, x_hat: torch.Tensor, stream=None):
     """[delta ; B ; C] = W_x x_hat; returns (delta (T, dt_rank), B (T, N) fp32, C (T, N) fp32)."""
     d, dt = layer.dims, _torch_dtype(layer.dims)
@@ -377,6 +400,7 @@ def jm_stage_x_proj(layer: MambaLayer, x_hat: torch.Tensor, stream=None):
     return delta, B, C
 
 
+@_on_call_stream
 def jm_stage_dt_proj(layer: MambaLayer, delta: torch.Tensor, stream=None):
     """Delta = softplus(W_dt delta + b_dt); returns (T, d_inner) fp32."""
     d, dt = layer.dims, _torch_dtype(layer.dims)
@@ -394,6 +418,7 @@ def jm_stage_scan_workspace_size(dims: LayerDims, total_tokens: int) -> int:
     return out.value
 
 
+@_on_call_stream
 def jm_stage_scan(layer: MambaLayer, x_hat: torch.Tensor, dt: torch.Tensor, B: torch.Tensor,
                   C: torch.Tensor, z: torch.Tensor, cu_seqlens: torch.Tensor,
                   cu_seqlens_host: Sequence[int], init_ssm_state=None,
@@ -422,6 +447,7 @@ def jm_stage_scan(layer: MambaLayer, x_hat: torch.Tensor, dt: torch.Tensor, B: t
     return g, fs
 
 
+@_on_call_stream
 def jm_stage_out_proj(layer: MambaLayer, g: torch.Tensor, stream=None):
     """out = W_out g; returns (T, d_model)."""
     d, dt = layer.dims, _torch_dtype(layer.dims)
@@ -431,6 +457,43 @@ def jm_stage_out_proj(layer: MambaLayer, g: torch.Tensor, stream=None):
     _check(lib().jm_stage_out_proj(ctypes.byref(d), ctypes.byref(layer.struct), _ptr(g), T,
                                    _ptr(out), _stream(stream)))
     return out
+
+
+@_on_call_stream
+def jm_stage_decode_update(layer: MambaLayer, x_hat: torch.Tensor, z: torch.Tensor,
+                           delta: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                           ssm_state: torch.Tensor, slots: Optional[Sequence[int]] = None,
+                           slots_device: Optional[torch.Tensor] = None, stream=None):
+    """Decode update (dt_proj + softplus + in-place state update + D skip + gate) for a batch
+    of one-token sequences; returns g (batch, d_inner). ssm_state is (batch, d_inner, N) fp32,
+    or with `slots` a cache (n_slots, d_inner, N) whose rows slots[b] are updated."""
+    d, at = layer.dims, _torch_dtype(layer.dims)
+    b = x_hat.shape[0] if x_hat.dim() == 2 else -1
+    di, N = d.d_inner, d.d_state
+    _need(x_hat, "x_hat", at, (b, di))
+    _need(z, "z", at, (b, di))
+    _need(delta, "delta", at, (b, d.dt_rank))
+    _need(B, "B", torch.float32, (b, N))
+    _need(C, "C", torch.float32, (b, N))
+    host, n_slots = None, 0
+    if slots is None:
+        _need(ssm_state, "ssm_state", torch.float32, (b, di, N))
+    else:
+        vals = [int(v) for v in slots]
+        if len(vals) != b:
+            raise ValueError(f"need {b} slot ids, got {len(vals)}")
+        n_slots = ssm_state.shape[0]
+        _need(ssm_state, "ssm_state", torch.float32, (n_slots, di, N))
+        host = (ctypes.c_int32 * b)(*vals)
+        if slots_device is None:
+            slots_device = torch.tensor(vals, dtype=torch.int32, device=x_hat.device)
+        _need(slots_device, "slots_device", torch.int32, (b,))
+    g = torch.empty_like(x_hat)
+    _check(lib().jm_stage_decode_update(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(x_hat), _ptr(z), _ptr(delta), _ptr(B),
+        _ptr(C), b, _ptr(slots_device) if slots is not None else None, host, n_slots,
+        _ptr(ssm_state), _ptr(g), _stream(stream)))
+    return g
 
 
 # ---- state cache (serving) ------------------------------------------------------------------
@@ -466,6 +529,7 @@ def prefill_slots_workspace_size(dims: LayerDims, n_seqs: int, total_tokens: int
     return out.value
 
 
+@_on_call_stream
 def jamba_mamba_prefill_slots(layer: MambaLayer, u: torch.Tensor, cu_seqlens: torch.Tensor,
                               cu_seqlens_host: Sequence[int], cache: StateCache,
                               init_slots=None, final_slots=None, out=None, workspace=None,
@@ -495,6 +559,7 @@ def jamba_mamba_prefill_slots(layer: MambaLayer, u: torch.Tensor, cu_seqlens: to
     return out
 
 
+@_on_call_stream
 def jamba_mamba_decode_step_slots(layer: MambaLayer, u: torch.Tensor, cache: StateCache,
                                   slots: Sequence[int], out=None, workspace=None, stream=None,
                                   slots_device: Optional[torch.Tensor] = None):
@@ -534,6 +599,7 @@ def jm_scan_backward_workspace_size(dims: LayerDims, total_tokens: int) -> int:
     return out.value
 
 
+@_on_call_stream
 def jamba_mamba_scan_backward(layer: MambaLayer, x_hat: torch.Tensor, dt: torch.Tensor,
                               B: torch.Tensor, C: torch.Tensor, z: torch.Tensor, dg: torch.Tensor,
                               cu_seqlens: torch.Tensor, cu_seqlens_host: Sequence[int],

@@ -19,7 +19,9 @@ using namespace jm;
 namespace {
 
 thread_local std::string g_last_error;
-int32_t g_chunk_override = 0;
+// Scan chunk-length override (jm_set_scan_chunk_len); read by every prefill, size query and
+// plan, so it is atomic (relaxed: it orders nothing else).
+std::atomic<int32_t> g_chunk_override{0};
 
 jm_status fail(jm_status s, const char* fmt, ...) {
   char buf[512];
@@ -151,8 +153,9 @@ int scan_block(int d_inner) { return d_inner % 256 == 0 ? 256 : (d_inner % 128 =
 
 void plan_chunks(const jm_layer_dims& d, int64_t T, int32_t* chunk_len, int32_t* n_chunks) {
   int64_t cl;
-  if (g_chunk_override > 0) {
-    cl = g_chunk_override;
+  const int32_t forced = g_chunk_override.load(std::memory_order_relaxed);
+  if (forced > 0) {
+    cl = forced;
   } else {
     // Aim for ~16384 workgroups across channel groups x chunks: 8 are resident per CU at a
     // time, and many short chunks (256 tokens for one 128K sequence at d_inner 8192) keep
@@ -361,6 +364,37 @@ jm_status run_prefill(const jm_layer_dims& d, const jm_layer_weights& w, const T
   return ok();
 }
 
+// Decode update for `b` rows: dt_proj + softplus + state update + D skip + gate (the fused
+// decode kernel; also exported on its own as jm_stage_decode_update). rows: state row (slot) of
+// each batch row, NULL = row i. The bf16 kernel takes at most 64 rows per launch.
+template <typename T>
+jm_status step_decode_update(const jm_layer_dims& d, const jm_layer_weights& w, const T* xh,
+                             const T* z, const T* delta, const float* Bm, const float* Cm,
+                             int32_t b, float* ssm_state, const int32_t* rows, T* g,
+                             hipStream_t stream) {
+  const int di = d.d_inner, R = d.dt_rank;
+  if constexpr (sizeof(T) == 2) {
+    if (decode_fast_path_ok(d.d_model, di, R)) {
+      for (int32_t b0 = 0; b0 < b; b0 += 64) {
+        const int M = b - b0 < 64 ? b - b0 : 64;
+        float* st = rows ? ssm_state : ssm_state + (int64_t)b0 * di * 16;
+        JM_LAUNCH("dec_update",
+                  launch_dec_update(xh + (int64_t)b0 * di, z + (int64_t)b0 * di,
+                                    delta + (int64_t)b0 * R, Bm + (int64_t)b0 * 16,
+                                    Cm + (int64_t)b0 * 16, static_cast<const bf16*>(w.dt_proj_w),
+                                    w.dt_proj_b, w.A_log, w.D, st, rows ? rows + b0 : nullptr,
+                                    g + (int64_t)b0 * di, M, di, R, stream));
+      }
+      return JM_OK;
+    }
+  }
+  JM_LAUNCH("dec_update",
+            launch_decode_update<T>(xh, z, delta, Bm, Cm, static_cast<const T*>(w.dt_proj_w),
+                                    w.dt_proj_b, w.A_log, w.D, ssm_state, rows, g, b, di, R,
+                                    stream));
+  return JM_OK;
+}
+
 // rows (device, batch entries) maps batch row -> state row (slot) of conv_state / ssm_state;
 // NULL: batch row b uses state row b.
 template <typename T>
@@ -399,10 +433,8 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
           JM_LAUNCH("dec_inner_norm",
                     launch_inner_rmsnorm<bf16>(delta, Bm, Cm, w.dt_norm_w, w.B_norm_w, w.C_norm_w,
                                                w.norm_eps, M, R, stream));
-        JM_LAUNCH("dec_update", launch_dec_update(xh, z, delta, Bm, Cm,
-                                                  static_cast<const bf16*>(w.dt_proj_w),
-                                                  w.dt_proj_b, w.A_log, w.D, st, rt, g, M, di,
-                                                  R, stream));
+        jm_status su = step_decode_update<bf16>(d, w, xh, z, delta, Bm, Cm, M, st, rt, g, stream);
+        if (su != JM_OK) return su;
         JM_LAUNCH("dec_out_proj", launch_dec_out_proj(g, static_cast<const bf16*>(w.out_proj_w),
                                                       partial, ot, M, dm, di, stream));
       }
@@ -410,6 +442,7 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
     }
   }
 
+  jm_status st;
   EpiArgs e = epi_none();
   e.kind = EPI_SPLIT2; e.out0 = x; e.out1 = z; e.split = di;
   JM_LAUNCH("dec_in_proj", gemm<T>(u, dm, static_cast<const T*>(w.in_proj_w), dm, b, 2 * di, dm,
@@ -424,10 +457,9 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
   if (w.dt_norm_w)
     JM_LAUNCH("dec_inner_norm", launch_inner_rmsnorm<T>(delta, Bm, Cm, w.dt_norm_w, w.B_norm_w,
                                                         w.C_norm_w, w.norm_eps, b, R, stream));
-  JM_LAUNCH("dec_update",
-            launch_decode_update<T>(xh, z, delta, Bm, Cm, static_cast<const T*>(w.dt_proj_w),
-                                    w.dt_proj_b, w.A_log, w.D, ssm_state, rows, g, b, di, R,
-                                    stream));
+  if ((st = step_decode_update<T>(d, w, xh, z, delta, Bm, Cm, b, ssm_state, rows, g, stream)) !=
+      JM_OK)
+    return st;
   e = epi_none();
   e.kind = EPI_STORE; e.out0 = out; e.ldo = dm;
   JM_LAUNCH("dec_out_proj", gemm<T>(g, di, static_cast<const T*>(w.out_proj_w), di, b, dm, di, e,
@@ -560,7 +592,7 @@ const char* jm_last_error(void) { return g_last_error.c_str(); }
 
 jm_status jm_set_scan_chunk_len(int32_t chunk_len) {
   if (chunk_len < 0) return fail(JM_ERR_INVALID_ARG, "chunk_len must be >= 0");
-  g_chunk_override = chunk_len;
+  g_chunk_override.store(chunk_len, std::memory_order_relaxed);
   return ok();
 }
 
@@ -923,6 +955,32 @@ jm_status jm_stage_out_proj(const jm_layer_dims* dims, const jm_layer_weights* w
                                           total_tokens, static_cast<bf16*>(out), s)
                      : step_out_proj<float>(*dims, *weights, static_cast<const float*>(g),
                                             total_tokens, static_cast<float*>(out), s);
+  return st == JM_OK ? ok() : st;
+}
+
+jm_status jm_stage_decode_update(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                                 const void* x_hat, const void* z, const void* delta,
+                                 const float* B, const float* C, int32_t batch,
+                                 const int32_t* slots, const int32_t* slots_host, int32_t n_slots,
+                                 float* ssm_state, void* g, void* stream) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK || (st = check_weights(weights)) != JM_OK) return st;
+  if (batch < 0) return fail(JM_ERR_INVALID_ARG, "negative batch");
+  if (batch == 0) return ok();
+  if ((st = check_ptrs({x_hat, z, delta, B, C, ssm_state, g})) != JM_OK) return st;
+  if (slots || slots_host) {
+    if (n_slots < 1) return fail(JM_ERR_INVALID_ARG, "n_slots < 1");
+    if ((st = check_decode_slots(slots, slots_host, batch, n_slots)) != JM_OK) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = is_bf16(dims)
+           ? step_decode_update<bf16>(*dims, *weights, static_cast<const bf16*>(x_hat),
+                                      static_cast<const bf16*>(z), static_cast<const bf16*>(delta),
+                                      B, C, batch, ssm_state, slots, static_cast<bf16*>(g), s)
+           : step_decode_update<float>(*dims, *weights, static_cast<const float*>(x_hat),
+                                       static_cast<const float*>(z),
+                                       static_cast<const float*>(delta), B, C, batch, ssm_state,
+                                       slots, static_cast<float*>(g), s);
   return st == JM_OK ? ok() : st;
 }
 

@@ -84,7 +84,7 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
     for (int r = 0; r < 16; ++r) { acc[f][0][r] = 0.0f; acc[f][1][r] = 0.0f; }
   // Register double buffer: the loads of block i+1 are in flight while block i's
   // MFMAs run. The steady-state loop has no branches, so the compiler can wait for
-  // exactly the older buffer (kw / 64 is even by construction).
+  // exactly the older buffer.
   struct Buf { bf16x8 w[FB][4], a[4], b[4]; };
   // Workgroups walk their K slice starting at different 64-wide blocks, so the
   // token rows (shared by every workgroup, served from L2) are not all requested
@@ -131,7 +131,8 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
     load(b3, (i << 6) + 192);
     compute(b0); compute(b1); compute(b2); compute(b3);
   } else {
-    // Two register buffers (nb is even).
+    // Two register buffers. The loop leaves one block (nb odd) or two (nb even) in flight;
+    // a load past the last block would wrap to block `rot` and count it twice.
     Buf b0, b1;
     load(b0, 0);
     int kk = 0;
@@ -139,9 +140,13 @@ void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int
       load(b1, kk + 64); compute(b0); order();
       load(b0, kk + 128); compute(b1); order();
     }
-    load(b1, kk + 64);
-    compute(b0);
-    compute(b1);
+    if (kk + 64 < kw) {
+      load(b1, kk + 64);
+      compute(b0);
+      compute(b1);
+    } else {
+      compute(b0);
+    }
   }
 #pragma unroll
   for (int f = 0; f < FB; ++f)

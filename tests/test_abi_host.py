@@ -203,6 +203,23 @@ def test_stage_validation_paths(L):
     assert L.jm_stage_scan(*args(None, None, None, need.value)) == S["JM_ERR_WORKSPACE"]
     assert L.jm_stage_scan(*args(0x50000000, 0x50000100, f(), need.value)) == S["JM_ERR_INVALID_ARG"]
     assert L.jm_stage_scan(*args(None, None, f(), need.value, h=bad, n=2, T=9)) == S["JM_ERR_SHAPE"]
+    # decode update: required pointers, alignment, batch, and the optional slot map
+    arr = lambda *v: (ctypes.c_int32 * len(v))(*v)  # noqa: E731
+
+    def upd(b, xh, slots=None, slots_host=None, n_slots=0, B=None):
+        return L.jm_stage_decode_update(D, W, xh, f(), f(), f() if B is None else B, f(), b,
+                                        slots, slots_host, n_slots, f(), f(), None)
+
+    assert upd(4, None) == S["JM_ERR_INVALID_ARG"]
+    assert upd(4, f() + 4) == S["JM_ERR_ALIGNMENT"]
+    assert upd(4, f(), B=f() + 8) == S["JM_ERR_ALIGNMENT"]
+    assert upd(-1, f()) == S["JM_ERR_INVALID_ARG"]
+    assert upd(0, None) == S["JM_OK"]
+    assert upd(3, f(), f(), arr(0, 8, 1), 8) == S["JM_ERR_SHAPE"]          # slot 8 of 8
+    assert upd(3, f(), f(), arr(2, 5, 2), 8) == S["JM_ERR_INVALID_ARG"]    # slot twice
+    assert upd(3, f(), None, arr(2, 5, 3), 8) == S["JM_ERR_INVALID_ARG"]   # no device copy
+    assert upd(3, f(), f(), None, 8) == S["JM_ERR_INVALID_ARG"]            # no host copy
+    assert upd(3, f(), f(), arr(2, 5, 3), 0) == S["JM_ERR_INVALID_ARG"]    # n_slots < 1
 
 
 def test_state_cache_validation_paths(L):

@@ -242,3 +242,42 @@ def test_prefill_state_equals_repeated_decode_fp32():
     torch.cuda.synchronize()
     assert np.array_equal(to_np(conv), conv_p)
     assert rel_err(to_np(ssm), ssm_p) < 1e-5
+
+
+@pytest.mark.parametrize("widths,batch,D_value", [
+    ((512, 1024, 128), 5, 0.0),     # out_proj: one 64-wide K block per wave
+    ((512, 1024, 128), 70, 1.0),
+    ((768, 3072, 128), 5, 1.0),     # in_proj and out_proj: three K blocks per wave
+    ((768, 3072, 128), 70, 0.0),    # and two 64-row tiles
+])
+def test_decode_bf16_odd_k_blocks(widths, batch, D_value):
+    """Widths at which a wave of the fast decode GEMM owns an odd number of 64-wide K blocks
+    (d_model / 256 or d_inner / 1024 odd): every block must enter the sum exactly once."""
+    dm, di, R = widths
+    dims = synth.LayerDims(d_model=dm, d_inner=di, d_state=16, d_conv=4, dt_rank=R)
+    wl = synth.make_workload("decode_b64", dims=dims, batch=batch, prefill_len=5, steps=3,
+                             D_value=D_value)
+    _decode_case(wl, 3, TOL["bf16"])
+
+
+def test_stream_argument_without_context_manager(jamba_small):
+    """stream= given while another stream is current: the result equals the same call on the
+    current stream, bit for bit (outputs and workspace belong to the call's stream)."""
+    wl = jamba_small[0.0]
+    layer = device_layer(wl)
+    base = gpu_prefill(wl, layer)
+    side = torch.cuda.Stream()
+    u = to_dev(wl.u, wl.dtype)
+    cu_d = torch.as_tensor(wl.cu_seqlens, dtype=torch.int32).cuda()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(3):   # later calls reuse memory the allocator gave earlier ones
+        res.append(jm.jamba_mamba_prefill(layer, u, cu_d, wl.cu_seqlens, stream=side))
+        junk = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        junk.fill_(0xAB)          # current-stream work that would clobber a shared workspace
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for out, conv, ssm in res:
+        assert np.array_equal(to_np(out), base[0])
+        assert np.array_equal(to_np(conv), base[1]) and np.array_equal(to_np(ssm), base[2])

@@ -24,8 +24,13 @@ jm = pytest.importorskip("mamba_selective_scan_mixer_amd")
 TOL = 1e-4
 
 
-def make_case(name, lengths, seed, with_states=True):
-    wl = synth.make_workload(name, lengths=[4])
+def make_case(name, lengths, seed, with_states=True, d_inner=None):
+    dims = None
+    if d_inner is not None:
+        base = synth.WORKLOADS[name]["dims"]
+        dims = synth.LayerDims(d_model=base.d_model, d_inner=d_inner, d_state=16, d_conv=4,
+                               dt_rank=base.dt_rank)
+    wl = synth.make_workload(name, lengths=[4], dims=dims)
     rng = np.random.default_rng(seed)
     di = wl.dims.d_inner
     T = int(sum(lengths))
@@ -90,6 +95,28 @@ def test_scan_backward_matches_oracle(name, lengths):
     errs = {k: rel_err(to_np(g[k]), ref[v]) for k, v in NAMES.items()}
     print(f"scan backward {name} {lengths}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()),
           flush=True)
+    assert max(errs.values()) < TOL, errs
+
+
+# Lengths past the 64-token chunk of the backward: the carry kernels take eight chunks per
+# step, so 18+ chunks run their loops three times. Borders of `BORDERS` fall on chunk edges
+# (64, 704, 832, 1152) and inside chunks (65, 833), with one-token sequences on both sides.
+BORDERS = [64, 1, 639, 128, 1, 319]
+
+
+@pytest.mark.parametrize("name,lengths,d_inner", [
+    ("tiny_fp32", BORDERS, 256),               # 1152 tokens, 18 chunks, fp32
+    ("tiny_fp32", [1300], 512),               # one sequence over 21 chunks
+    ("prefill_4k", [1, 1150, 3], 256),        # bf16 activations, 18 chunks
+    ("prefill_4k", [300, 1, 299], None),      # Jamba widths (d_inner 8192), bf16, 10 chunks
+])
+def test_scan_backward_many_chunks(name, lengths, d_inner):
+    wl, c, cu = make_case(name, lengths, seed=len(lengths) + sum(lengths), d_inner=d_inner)
+    g = run(wl, c, cu)
+    ref = reference(wl, c, cu)
+    errs = {k: rel_err(to_np(g[k]), ref[v]) for k, v in NAMES.items()}
+    print(f"scan backward {name} d_inner={wl.dims.d_inner} {lengths}: "
+          + " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
     assert max(errs.values()) < TOL, errs
 
 

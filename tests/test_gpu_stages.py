@@ -207,3 +207,85 @@ def test_stages_compose_to_prefill(case):
     assert torch.equal(out, out_ref)
     assert torch.equal(fc, conv_ref)
     assert torch.equal(fs, ssm_ref)
+
+
+def _decode_update_inputs(wl, w):
+    """The decode update's upstream tensors for one step, from the oracle's own steps: states
+    from the oracle's prefill of the workload, then in_proj, conv + SiLU (each sequence from its
+    carried window) and x_proj of the step's tokens; rounded to the dtypes the kernel reads."""
+    di, R, N = wl.dims.d_inner, wl.dims.dt_rank, wl.dims.d_state
+    ref = oracle.prefill(w, wl.u, wl.cu_seqlens)
+    tok = wl.next_decode_tokens()
+    x, z = oracle.in_proj(tok, w["in_proj_w"], di)
+    xh = np.empty_like(x)
+    for b in range(wl.n_seqs):
+        xh[b:b + 1], _ = oracle.causal_conv_silu(x[b:b + 1], w["conv_w"], w["conv_b"],
+                                                 ref["conv_state"][b])
+    delta, B, C = oracle.x_proj(xh, w["x_proj_w"], R, N)
+    f32 = lambda a: a.astype(np.float32).astype(np.float64)  # noqa: E731
+    return dict(xh=_round(xh, wl.dtype), z=_round(z, wl.dtype), delta=_round(delta, wl.dtype),
+                B=f32(B), C=f32(C), h0=f32(ref["ssm_state"]))
+
+
+def _decode_update_reference(w, c):
+    """dt_proj + softplus, one step of the recurrence from each sequence's state, D skip and
+    gate: the oracle's own step functions with T = 1 per sequence."""
+    dt = oracle.dt_proj(c["delta"], w["dt_proj_w"], w["dt_proj_b"])
+    A = -np.exp(w["A_log"])
+    g = np.empty_like(c["xh"])
+    h = np.empty_like(c["h0"])
+    for b in range(c["xh"].shape[0]):
+        y, h[b] = oracle.selective_scan(c["xh"][b:b + 1], dt[b:b + 1], A, c["B"][b:b + 1],
+                                        c["C"][b:b + 1], w["D"], c["h0"][b])
+        g[b:b + 1] = oracle.gate(y, c["z"][b:b + 1])
+    return g, h
+
+
+@pytest.mark.parametrize("batch,use_slots,D_value", [
+    (64, False, 0.0), (64, False, 1.0), (70, True, 0.0), (70, False, 1.0), (5, True, 1.0)])
+def test_stage_decode_update(batch, use_slots, D_value):
+    """jm_stage_decode_update (the fused decode kernel: dt_proj on MFMA, softplus, in-place state
+    update, D skip, gate) at Jamba widths, one and two 64-row tiles, with and without a slot map
+    (slots outside the batch must stay bit-for-bit unchanged)."""
+    wl = synth.make_workload("decode_b64", batch=batch, prefill_len=6, steps=1, D_value=D_value)
+    _check_decode_update(wl, use_slots)
+
+
+def test_stage_decode_update_generic_fp32():
+    """The fp32 layer's decode update (generic kernel), tiny widths."""
+    wl = synth.make_workload("decode_b64", dims=synth.TINY_DIMS, dtype="f32", batch=5,
+                             prefill_len=7, steps=1, D_value=0.0)
+    _check_decode_update(wl, use_slots=True)
+
+
+def _check_decode_update(wl, use_slots):
+    layer = device_layer(wl)
+    w = oracle.as_f64(wl.weights)
+    c = _decode_update_inputs(wl, w)
+    g_ref, h_ref = _decode_update_reference(w, c)
+    b, di = c["xh"].shape
+    dev = lambda k, dt: to_dev(c[k], dt)  # noqa: E731
+    args = (layer, dev("xh", wl.dtype), dev("z", wl.dtype), dev("delta", wl.dtype),
+            dev("B", "f32"), dev("C", "f32"))
+    if use_slots:
+        n_slots = 2 * b + 3
+        rng = np.random.default_rng(b)
+        slots = [int(v) for v in rng.permutation(n_slots)[:b]]
+        cache = torch.as_tensor((rng.standard_normal((n_slots, di, 16)) * 0.01).astype(np.float32)).cuda()
+        cache[torch.as_tensor(slots, dtype=torch.long).cuda()] = to_dev(c["h0"], "f32")
+        before = cache.clone()
+        g = jm.jm_stage_decode_update(*args, cache, slots=slots)
+        torch.cuda.synchronize()
+        h = to_np(cache[torch.as_tensor(slots, dtype=torch.long).cuda()])
+        others = sorted(set(range(n_slots)) - set(slots))
+        idx = torch.as_tensor(others, dtype=torch.long).cuda()
+        assert torch.equal(cache[idx], before[idx]), "a slot outside the batch changed"
+    else:
+        state = to_dev(c["h0"], "f32")
+        g = jm.jm_stage_decode_update(*args, state)
+        torch.cuda.synchronize()
+        h = to_np(state)
+    e = dict(g=rel_err(to_np(g), g_ref), state=rel_err(h, h_ref))
+    print(f"decode update {wl.dtype} batch={b} slots={use_slots}: {e}", flush=True)
+    assert e["g"] < _out_tol(wl.dtype, "scan"), e
+    assert e["state"] < F32_SCAN, e

@@ -564,3 +564,26 @@ def test_planted_scan_kernel_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(ref, "selective_scan", wrong)
     monkeypatch.setattr(oracle, "selective_scan", wrong)
     assert _fails_some_pin()
+
+
+def test_blocked_prefill_equals_one_call():
+    """The test helper that streams the oracle's prefill in token blocks (carrying each
+    sequence's states between blocks) gives the one-call prefill: outputs and final states."""
+    from jm_testutil import oracle_prefill_blocked
+    wl = synth.make_workload("tiny_fp32", seed=11, lengths=[20, 3, 9, 1])
+    w = oracle.as_f64(wl.weights)
+    rng = np.random.default_rng(12)
+    ic = rng.standard_normal((4, 128, 3))
+    ih = rng.standard_normal((4, 128, 16)) * 0.1
+    ref = oracle.prefill(w, wl.u, wl.cu_seqlens, ic, ih)
+    got = np.full_like(ref["out"], np.nan)
+
+    def put(r0, rows):
+        got[r0:r0 + len(rows)] = rows
+
+    conv, ssm = oracle_prefill_blocked(oracle, w, wl.u, wl.cu_seqlens, 7, put, ic, ih)
+    assert np.max(np.abs(got - ref["out"])) <= 1e-12 * np.max(np.abs(ref["out"]))
+    # conv state: copies of x, whose in_proj products BLAS may round differently for a
+    # different number of rows, so the same 1e-12 bound as the other tensors
+    assert np.max(np.abs(conv - ref["conv_state"])) <= 1e-12 * np.max(np.abs(ref["conv_state"]))
+    assert np.max(np.abs(ssm - ref["ssm_state"])) <= 1e-12 * np.max(np.abs(ref["ssm_state"]))

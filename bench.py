@@ -110,9 +110,21 @@ def cpu_baseline(wl, target_s: float = 15.0):
     oracle.prefill(w64, wl.u[:n], [0, n])
     el = time.perf_counter() - t
     return {"value": n / el, "unit": "tokens/s", "cores": int(max(blas_threads, omp)),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "cpu_count": os.cpu_count(),
             "sample": f"first {n} tokens of the 131072-token sequence, fp64 oracle (numpy matmul "
                       f"+ C recurrence), {el:.1f} s wall; BLAS threads {blas_threads}, OpenMP {omp}"}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (what lscpu reports), from /proc/cpuinfo."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -127,6 +139,9 @@ def main():
     ap.add_argument("--no-inner-norm", action="store_true",
                     help="skip the prefill measurement with the inner RMSNorm on")
     ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the timed prefill (profiling runs of the other legs; the line's "
+                         "value is then null)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -162,74 +177,75 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    def step():
-        jm.jamba_mamba_prefill(layer, u, cu, wl.cu_seqlens, out=out, final_conv_state=fconv,
-                               final_ssm_state=fssm, workspace=ws)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    jm.profile_reset()
-    jm.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    jm.profile_enable(False)
-    prof = jm.profile_read()
-    jm.profile_reset()
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = T * args.steps / elapsed
-    print(f"[bench] prefill {ms_per_step:.2f} ms/step, {value / 1e6:.3f} M tok/s", file=sys.stderr,
-          flush=True)
-
-    cl, nc, _ = jm.prefill_plan(dims, wl.cu_seqlens)
-    work = kernel_work(T, d.d_model, d.d_inner, d.dt_rank)
-    work["scan_chunk_carry"] = (0.0, 3.0 * nc * d.d_inner * 16 * 4)
+    value = ms_per_step = roof = None
     kernels = {}
-    for name, (launches, total_ms) in prof.items():
-        avg = total_ms / max(launches, 1)
-        flops, nbytes = work.get(name, (0.0, 0.0))
-        k = {"launches": launches, "avg_ms": round(avg, 4),
-             "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1) if nbytes else None,
-             "tflops": round(flops / (avg * 1e-3) / 1e12, 1) if flops else None}
-        b = bound_of(name)
-        k["bound"] = b
-        if name in SCAN_SLOTS:
-            updates = float(T) * d.d_inner * 16
-            if name == "scan_chunk_state":
-                updates *= (nc - 1) / nc      # the last chunk needs no aggregate
-            k["alu_frac"] = round(updates * SCAN_SLOTS[name] / VALU_LANE_OPS / (avg * 1e-3), 4)
-        if b == "mfma":
-            k["frac"] = round(k["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
-        elif b == "alu":
-            k["frac"] = k["alu_frac"]
-        elif k["gbs"] is not None:
-            k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
-        kernels[name] = k
-    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"]) if kernels else None
-    roof = None
-    if dom:
-        kd = kernels[dom]
-        if kd["bound"] == "mfma":
-            roof = {"kernel": dom, "bound": "mfma", "achieved": kd["tflops"],
-                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
-                    "traffic": recorded_traffic(dom),
-                    "traffic_note": "HBM-side bytes per launch = 2 x FETCH_SIZE + WRITE_SIZE "
-                                    "(calibrated on a 1 GiB copy); algorithmic bytes "
-                                    f"{kernel_work(T, d.d_model, d.d_inner, d.dt_rank)[dom][1]:.4g}"}
-        elif kd["bound"] == "alu":
-            roof = {"kernel": dom, "bound": "alu", "achieved": kd["alu_frac"] * VALU_LANE_OPS / 1e12,
-                    "peak": VALU_LANE_OPS / 1e12, "unit": "T VALU lane-slots/s",
-                    "frac": kd["alu_frac"], "traffic": None}
-        else:
-            roof = {"kernel": dom, "bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": kd["frac"], "traffic": None}
+    cl, nc, _ = jm.prefill_plan(dims, wl.cu_seqlens)
+    if not args.no_prefill:
+        def step():
+            jm.jamba_mamba_prefill(layer, u, cu, wl.cu_seqlens, out=out, final_conv_state=fconv,
+                                   final_ssm_state=fssm, workspace=ws)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        jm.profile_reset()
+        jm.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        jm.profile_enable(False)
+        prof = jm.profile_read()
+        jm.profile_reset()
+        ms_per_step = elapsed * 1e3 / args.steps
+        value = T * args.steps / elapsed
+        print(f"[bench] prefill {ms_per_step:.2f} ms/step, {value / 1e6:.3f} M tok/s", file=sys.stderr,
+              flush=True)
+
+        work = kernel_work(T, d.d_model, d.d_inner, d.dt_rank)
+        work["scan_chunk_carry"] = (0.0, 3.0 * nc * d.d_inner * 16 * 4)
+        for name, (launches, total_ms) in prof.items():
+            avg = total_ms / max(launches, 1)
+            flops, nbytes = work.get(name, (0.0, 0.0))
+            k = {"launches": launches, "avg_ms": round(avg, 4),
+                 "gbs": round(nbytes / (avg * 1e-3) / 1e9, 1) if nbytes else None,
+                 "tflops": round(flops / (avg * 1e-3) / 1e12, 1) if flops else None}
+            b = bound_of(name)
+            k["bound"] = b
+            if name in SCAN_SLOTS:
+                updates = float(T) * d.d_inner * 16
+                if name == "scan_chunk_state":
+                    updates *= (nc - 1) / nc      # the last chunk needs no aggregate
+                k["alu_frac"] = round(updates * SCAN_SLOTS[name] / VALU_LANE_OPS / (avg * 1e-3), 4)
+            if b == "mfma":
+                k["frac"] = round(k["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+            elif b == "alu":
+                k["frac"] = k["alu_frac"]
+            elif k["gbs"] is not None:
+                k["frac"] = round(k["gbs"] / HBM_PEAK_GBS, 4)
+            kernels[name] = k
+        dom = max(kernels, key=lambda n: kernels[n]["avg_ms"]) if kernels else None
+        if dom:
+            kd = kernels[dom]
+            if kd["bound"] == "mfma":
+                roof = {"kernel": dom, "bound": "mfma", "achieved": kd["tflops"],
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
+                        "traffic": recorded_traffic(dom),
+                        "traffic_note": "HBM-side bytes per launch = 2 x FETCH_SIZE + WRITE_SIZE "
+                                        "(calibrated on a 1 GiB copy); algorithmic bytes "
+                                        f"{kernel_work(T, d.d_model, d.d_inner, d.dt_rank)[dom][1]:.4g}"}
+            elif kd["bound"] == "alu":
+                roof = {"kernel": dom, "bound": "alu", "achieved": kd["alu_frac"] * VALU_LANE_OPS / 1e12,
+                        "peak": VALU_LANE_OPS / 1e12, "unit": "T VALU lane-slots/s",
+                        "frac": kd["alu_frac"], "traffic": None}
+            else:
+                roof = {"kernel": dom, "bound": "hbm", "achieved": kd["gbs"], "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": kd["frac"], "traffic": None}
 
     inner = None
-    if not args.no_inner_norm:
+    if not args.no_inner_norm and not args.no_prefill:
         inner = run_inner_norm(jm, torch, wl, dims, u, cu, out, fconv, fssm, ws, T)
         print(f"[bench] prefill with inner norm {inner['ms_per_step']:.2f} ms/step "
               f"(norm kernel {inner['norm_kernel']['avg_ms']:.3f} ms)", file=sys.stderr, flush=True)
@@ -253,8 +269,9 @@ def main():
               flush=True)
 
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "metric": METRIC, "value": None if value is None else round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None if ms_per_step is None else round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "prefill_128k: one 131072-token sequence, Mamba layer d_model 4096, "

@@ -153,6 +153,28 @@ jm_status jamba_mamba_decode_step(const jm_layer_dims *dims, const jm_layer_weig
                                   float *ssm_state, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* Bytes of the fixed device-side scratch that jamba_mamba_decode_step_noalloc uses on each
+ * GPU (32 MiB: a decode step at the Jamba-7B-class sizes needs about 4.2 MB plus 64 KB per
+ * sequence, so batches up to about 440 fit). */
+#define JM_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * jamba_mamba_decode_step without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The step's temporaries live in a fixed device-side scratch array of
+ * JM_DECODE_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the process
+ * ends; the call allocates nothing (the first call on a device only looks up that device's
+ * copy, a runtime query). Arguments and results as jamba_mamba_decode_step; the device of
+ * `stream` must be the current device. A batch whose jm_decode_workspace_size exceeds the
+ * scratch returns JM_ERR_WORKSPACE with nothing enqueued. All calls on one GPU share its one
+ * scratch array: calls that overlap on one GPU (other streams or threads) race and must be
+ * ordered by the caller.
+ */
+jm_status jamba_mamba_decode_step_noalloc(const jm_layer_dims *dims,
+                                          const jm_layer_weights *weights, const void *u,
+                                          int32_t batch, void *conv_state, float *ssm_state,
+                                          void *out, void *stream);
+
 /* ---- State cache (serving) ------------------------------------------------------------
  * The per-sequence state is what replaces the KV cache (Jamba paper §2, the KV-cache
  * paragraph and Table 1; §3.1: long contexts on one 80 GB GPU). A server keeps the states

@@ -118,6 +118,9 @@ def lib() -> ctypes.CDLL:
         L.jamba_mamba_scan_backward.argtypes = [
             D, W, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64, _P, _P,
             _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.jamba_mamba_decode_step_noalloc.argtypes = [
+            ctypes.POINTER(LayerDims), ctypes.POINTER(LayerWeights), _P, ctypes.c_int32, _P, _P,
+            _P, _P]
         L.jm_stage_decode_update.argtypes = [D, W, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                              ctypes.c_int32, _P, _P, _P]
         L.jamba_mamba_decode_step_slots.argtypes = [
@@ -127,7 +130,7 @@ def lib() -> ctypes.CDLL:
                      "jm_profile_enable", "jm_profile_reset", "jm_profile_read",
                      "jm_stage_in_proj", "jm_stage_conv", "jm_stage_x_proj", "jm_stage_dt_proj",
                      "jm_stage_scan_workspace_size", "jm_stage_scan", "jm_stage_out_proj",
-                     "jm_stage_decode_update",
+                     "jm_stage_decode_update", "jamba_mamba_decode_step_noalloc",
                      "jm_prefill_slots_workspace_size", "jamba_mamba_prefill_slots",
                      "jamba_mamba_decode_step_slots", "jm_scan_backward_workspace_size",
                      "jamba_mamba_scan_backward"):
@@ -312,6 +315,28 @@ def jamba_mamba_decode_step(layer: MambaLayer, u: torch.Tensor, conv_state: torc
     _check(lib().jamba_mamba_decode_step(
         ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), b, _ptr(conv_state),
         _ptr(ssm_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # JM_DECODE_NOALLOC_SCRATCH_BYTES
+
+
+@_on_call_stream
+def jamba_mamba_decode_step_noalloc(layer: MambaLayer, u: torch.Tensor, conv_state: torch.Tensor,
+                                    ssm_state: torch.Tensor, out: torch.Tensor, stream=None):
+    """jamba_mamba_decode_step without a workspace: the library uses its fixed per-GPU scratch
+    and allocates nothing (neither does this wrapper: `out` is the caller's). Calls that overlap
+    on one GPU race on that scratch. Updates the states in place; returns out."""
+    d = layer.dims
+    dt = _torch_dtype(d)
+    b = u.shape[0] if u.dim() == 2 else -1
+    _need(u, "u", dt, (b, d.d_model))
+    _need(conv_state, "conv_state", dt, (b, d.d_inner, d.d_conv - 1))
+    _need(ssm_state, "ssm_state", torch.float32, (b, d.d_inner, d.d_state))
+    _need(out, "out", dt, (b, d.d_model))
+    _check(lib().jamba_mamba_decode_step_noalloc(
+        ctypes.byref(d), ctypes.byref(layer.struct), _ptr(u), b, _ptr(conv_state),
+        _ptr(ssm_state), _ptr(out), _stream(stream)))
     return out
 
 

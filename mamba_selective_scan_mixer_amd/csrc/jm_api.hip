@@ -16,6 +16,10 @@
 
 using namespace jm;
 
+// Fixed scratch of jamba_mamba_decode_step_noalloc: the decode step's temporaries (no
+// kernel reads any of it before writing it, so it needs no clearing between calls).
+static __device__ __align__(256) unsigned char scratch[JM_DECODE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -571,6 +575,64 @@ jm_status run_scan_backward(const jm_layer_dims& d, const jm_layer_weights& wt, 
   return JM_OK;
 }
 
+// ---- decode: shared validation and dispatch ------------------------------------------------
+jm_status check_decode_args(const jm_layer_dims* dims, const jm_layer_weights* weights,
+                            const void* u, int32_t batch, const void* conv_state,
+                            const float* ssm_state, const void* out) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if ((st = check_weights(weights)) != JM_OK) return st;
+  if (batch < 0) return fail(JM_ERR_INVALID_ARG, "negative batch");
+  if (batch == 0) return JM_OK;
+  if (!u || !conv_state || !ssm_state || !out)
+    return fail(JM_ERR_INVALID_ARG, "u, conv_state, ssm_state and out must not be NULL");
+  const void* ptrs[] = {u, conv_state, ssm_state, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  return JM_OK;
+}
+
+jm_status dispatch_decode(const jm_layer_dims& d, const jm_layer_weights& w, const void* u,
+                          int32_t batch, void* conv_state, float* ssm_state, void* out, char* ws,
+                          hipStream_t s) {
+  if (d.act_dtype == JM_BF16)
+    return run_decode<bf16>(d, w, static_cast<const bf16*>(u), batch,
+                            static_cast<bf16*>(conv_state), ssm_state, static_cast<bf16*>(out),
+                            ws, s);
+  return run_decode<float>(d, w, static_cast<const float*>(u), batch,
+                           static_cast<float*>(conv_state), ssm_state, static_cast<float*>(out),
+                           ws, s);
+}
+
+// ---- fixed device-side scratch (decode without a caller workspace) -------------------------
+// Each GPU holds its own copy of `scratch` at its own address. Host code never passes the
+// array's name to a kernel or a copy (on the host that name is only a stand-in): the address
+// is looked up once per device, with that device current, and kept.
+constexpr size_t kScratchBytes = JM_DECODE_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+std::atomic<char*> g_scratch_ptr[kScratchDevices];
+
+jm_status scratch_for_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(JM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(JM_ERR_UNSUPPORTED, "device %d: the fixed scratch serves devices 0..%d", dev,
+                kScratchDevices - 1);
+  char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !addr)
+      return fail(JM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    p = static_cast<char*>(addr);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);   // same value from any thread
+  }
+  *out = p;
+  return JM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -718,30 +780,32 @@ jm_status jamba_mamba_decode_step(const jm_layer_dims* dims, const jm_layer_weig
                                   const void* u, int32_t batch, void* conv_state,
                                   float* ssm_state, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream_ptr) {
-  jm_status st = check_dims(dims);
-  if (st != JM_OK) return st;
-  st = check_weights(weights);
-  if (st != JM_OK) return st;
-  if (batch < 0) return fail(JM_ERR_INVALID_ARG, "negative batch");
-  if (batch == 0) return ok();
-  if (!u || !conv_state || !ssm_state || !out)
-    return fail(JM_ERR_INVALID_ARG, "u, conv_state, ssm_state and out must not be NULL");
-  const void* ptrs[] = {u, conv_state, ssm_state, out, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  jm_status st = check_decode_args(dims, weights, u, batch, conv_state, ssm_state, out);
+  if (st != JM_OK || batch == 0) return st == JM_OK ? ok() : st;
+  if (workspace && !aligned16(workspace))
+    return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
   const size_t need = decode_layout(*dims, batch).total;
   if (!workspace || workspace_bytes < need)
     return fail(JM_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
                 workspace ? workspace_bytes : (size_t)0);
-  hipStream_t s = static_cast<hipStream_t>(stream_ptr);
-  char* ws = static_cast<char*>(workspace);
-  if (dims->act_dtype == JM_BF16)
-    return run_decode<bf16>(*dims, *weights, static_cast<const bf16*>(u), batch,
-                            static_cast<bf16*>(conv_state), ssm_state, static_cast<bf16*>(out),
-                            ws, s);
-  return run_decode<float>(*dims, *weights, static_cast<const float*>(u), batch,
-                           static_cast<float*>(conv_state), ssm_state, static_cast<float*>(out), ws,
-                           s);
+  return dispatch_decode(*dims, *weights, u, batch, conv_state, ssm_state, out,
+                         static_cast<char*>(workspace), static_cast<hipStream_t>(stream_ptr));
+}
+
+jm_status jamba_mamba_decode_step_noalloc(const jm_layer_dims* dims,
+                                          const jm_layer_weights* weights, const void* u,
+                                          int32_t batch, void* conv_state, float* ssm_state,
+                                          void* out, void* stream_ptr) {
+  jm_status st = check_decode_args(dims, weights, u, batch, conv_state, ssm_state, out);
+  if (st != JM_OK || batch == 0) return st == JM_OK ? ok() : st;
+  const size_t need = decode_layout(*dims, batch).total;
+  if (need > kScratchBytes)
+    return fail(JM_ERR_WORKSPACE, "batch %d needs %zu bytes of scratch; the fixed scratch holds "
+                "%zu", batch, need, kScratchBytes);
+  char* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != JM_OK) return st;
+  return dispatch_decode(*dims, *weights, u, batch, conv_state, ssm_state, out, ws,
+                         static_cast<hipStream_t>(stream_ptr));
 }
 
 // ---- state-cache (slot) entry points -----------------------------------------------------

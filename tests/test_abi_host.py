@@ -168,6 +168,27 @@ def test_decode_validation_paths(L):
     assert call(0, None, None, None, None, None, 0) == S["JM_OK"]
 
 
+def test_noalloc_decode_validation_paths(L):
+    """The no-workspace decode step validates like the decode step and rejects a batch whose
+    workspace would not fit the fixed scratch, all before touching the GPU."""
+    f = _Fake()
+    d = dims()
+    w = _weights(f)
+    S = {n: i for i, n in enumerate(jm._STATUS)}
+    call = lambda b, u=None: L.jamba_mamba_decode_step_noalloc(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(w), f() if u is None else u, b, f(), f(), f(), None)
+    fits = max(b for b in range(1, 1024) if jm.decode_workspace_size(d, b) <= jm.NOALLOC_SCRATCH_BYTES)
+    assert 400 < fits < 1024
+    assert call(fits + 1) == S["JM_ERR_WORKSPACE"]
+    assert call(4096) == S["JM_ERR_WORKSPACE"]
+    assert call(-1) == S["JM_ERR_INVALID_ARG"]
+    assert call(4, u=f() + 8) == S["JM_ERR_ALIGNMENT"]
+    assert L.jamba_mamba_decode_step_noalloc(ctypes.byref(d), ctypes.byref(w), None, 4, f(), f(),
+                                             f(), None) == S["JM_ERR_INVALID_ARG"]
+    assert L.jamba_mamba_decode_step_noalloc(ctypes.byref(d), ctypes.byref(w), None, 0, None,
+                                             None, None, None) == S["JM_OK"]
+
+
 def test_stage_validation_paths(L):
     """Every stage entry point rejects bad arguments on the host (nothing is launched)."""
     f = _Fake()

@@ -4,26 +4,24 @@
 // At one token per sequence every projection is a skinny (M <= 64) product whose
 // cost is streaming the weights (210 MB per step at the Jamba-7B-class sizes), so
 // the kernels here are built for bandwidth:
-//   dec_gemm      32 output features per workgroup; each wave takes a K slice and
-//                 loads weight rows and token rows straight into MFMA operand
-//                 registers (no LDS staging): a lane reads 64 contiguous bytes of a
-//                 row, and A and B use the same permutation of k, so the products
-//                 pair up correctly. Partial sums of the waves are combined in LDS
-//                 in a fixed order (deterministic). Optional split-K over a second
-//                 grid dimension writes fp32 partials.
+//   dec_gemm_lds  64 output features x 64 tokens per workgroup, optional split-K over a
+//                 second grid dimension (fp32 partials). Weight and token rows reach LDS
+//                 through direct-to-LDS loads of whole 128-byte row segments, 7 stages of
+//                 64 K columns in flight; each wave owns a 32 x 32 output tile.
 //   in_proj epilogue: the conv-state shift, the causal conv (kernel 4) and SiLU are
 //                 applied right there for the x half; the z half is stored.
-//   xproj_reduce  sums the split-K partials of x_proj in a fixed order.
-//   update        per 32 channels x 16 sequences: dt_proj on MFMA, softplus, the
-//                 16-state update in place, the D skip and the SiLU(z) gate.
+//   xproj_reduce, sum_partials: the split-K partial sums, added in a fixed order.
+//   update        per 32 channels x 16 sequences: dt_proj on MFMA (W_dt and delta rows
+//                 staged in LDS), softplus, the 16-state update in place, the D skip and
+//                 the SiLU(z) gate.
 #include "jm_internal.h"
+
+#include <atomic>
 
 namespace jm {
 namespace {
 
 constexpr int NS = 16;
-constexpr int DEC_NB = 32;   // output features per workgroup
-constexpr int DEC_MT = 64;   // token rows per launch
 
 enum DecEpi : int { DEC_STORE = 0, DEC_INPROJ_CONV = 1, DEC_PARTIAL = 2 };
 
@@ -39,210 +37,237 @@ struct DecEpiArgs {
   float* partial;        // PARTIAL: (splits, M, N) fp32
 };
 
-__device__ __forceinline__ void load64B(const bf16* p, bf16x8 v[4]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
+// ---- write-out of one item: token m, features n .. n+7 (n % 8 == 0) ------------------------
+// STORE: bf16 outputs; PARTIAL: fp32 split-K partial sums of split `split`.
+template <int EPI>
+__device__ __forceinline__ void dec_store_item(const DecEpiArgs& e, int m, int n, int N, int M,
+                                               int split, const float v[8]) {
+  const bool whole = n + 8 <= N;
+  if constexpr (EPI == DEC_STORE) {
+    if (whole) {
+      bf16x8 o;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    uint4 r = q[j];
-    v[j] = *reinterpret_cast<bf16x8*>(&r);
+      for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(v[c]);
+      *reinterpret_cast<bf16x8*>(e.out + (int64_t)m * N + n) = o;
+    } else {
+      for (int c = 0; c < 8 && n + c < N; ++c) e.out[(int64_t)m * N + n + c] = from_f32<bf16>(v[c]);
+    }
+  } else {
+    float* dst = e.partial + ((int64_t)split * M + m) * N + n;
+    if (whole) {
+      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+      for (int c = 0; c < 8 && n + c < N; ++c) dst[c] = v[c];
+    }
   }
 }
 
-template <int WAVES, int FB, int EPI>
-__global__ __launch_bounds__(64 * WAVES)
-void dec_gemm_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int M, int N, int K,
-                     int k_per_split, DecEpiArgs e) {
-  constexpr int NB = 32 * FB;                   // output features per workgroup
-  __shared__ float red[WAVES][FB * 2][16][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * NB;
-  const int split = blockIdx.y;
-  const int kbeg = split * k_per_split;
-  const int kw = k_per_split / WAVES;          // multiple of 64
-  const int ka = kbeg + wave * kw;
-  const int lrow = lane & 31;
-  const int half = lane >> 5;
+// in_proj items of the x half (n < d_inner) read the token's conv-state row (48 bytes), the taps
+// (64 bytes) and the bias (16 bytes) of their 8 features; z items read nothing.
+__device__ __forceinline__ void dec_inproj_load(const DecEpiArgs& e, int m, int n, bf16x8 s3[3],
+                                                bf16x8 w4[4], bf16x8& b8) {
+  const int di = e.d_inner;
+  if (n >= di) return;
+  const int64_t row = e.rows ? (int64_t)e.rows[m] : (int64_t)m;
+  const bf16x8* st = reinterpret_cast<const bf16x8*>(e.conv_state + (row * di + n) * 3);
+  const bf16x8* cw = reinterpret_cast<const bf16x8*>(e.conv_w + (int64_t)n * 4);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) s3[k] = st[k];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w4[k] = cw[k];
+  if (e.conv_b) b8 = *reinterpret_cast<const bf16x8*>(e.conv_b + n);
+}
 
-  const bf16* wp[FB];
-#pragma unroll
-  for (int f = 0; f < FB; ++f) {
-    int wrow = n0 + f * 32 + lrow;
-    if (wrow >= N) wrow = N - 1;               // clamped rows are never stored
-    wp[f] = W + (int64_t)wrow * K + ka + half * 32;
-  }
-  // Token rows past M read row 0 instead: an MFMA output column depends only on
-  // its own token's operand, and columns >= M are never stored.
-  const int t0 = lrow, t1 = lrow + 32;
-  const bf16* up0 = U + (int64_t)(t0 < M ? t0 : 0) * K + ka + half * 32;
-  const bf16* up1 = U + (int64_t)(t1 < M ? t1 : 0) * K + ka + half * 32;
-
-  f32x16 acc[FB][2];
-#pragma unroll
-  for (int f = 0; f < FB; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { acc[f][0][r] = 0.0f; acc[f][1][r] = 0.0f; }
-  // Register double buffer: the loads of block i+1 are in flight while block i's
-  // MFMAs run. The steady-state loop has no branches, so the compiler can wait for
-  // exactly the older buffer.
-  struct Buf { bf16x8 w[FB][4], a[4], b[4]; };
-  // Workgroups walk their K slice starting at different 64-wide blocks, so the
-  // token rows (shared by every workgroup, served from L2) are not all requested
-  // from the same few cache lines at the same moment.
-  const int nblk = kw >> 6;
-  const int rot = blockIdx.x % nblk;
-  auto load = [&](Buf& B, int kk) {
-    int blk = (kk >> 6) + rot;
-    if (blk >= nblk) blk -= nblk;
-    const int ko = blk << 6;
-#pragma unroll
-    for (int f = 0; f < FB; ++f) load64B(wp[f] + ko, B.w[f]);
-    load64B(up0 + ko, B.a);
-    load64B(up1 + ko, B.b);
-  };
-  auto compute = [&](const Buf& B) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        acc[f][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B.w[f][j], B.a[j], acc[f][0], 0, 0, 0);
-        acc[f][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(B.w[f][j], B.b[j], acc[f][1], 0, 0, 0);
-      }
-  };
-  constexpr int NLOAD = FB * 4 + 8;   // 16-byte loads per block
-  constexpr int NMFMA = FB * 8;       // MFMAs per block
-  auto order = [&]() {                // next blocks' loads first, then this block's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x020, NLOAD, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, NMFMA, 0);
-  };
-  const int nb = kw >> 6;
-  if (nb % 4 == 0) {
-    // Four register buffers: blocks i+1..i+3 are in flight while block i computes.
-    Buf b0, b1, b2, b3;
-    load(b0, 0); load(b1, 64); load(b2, 128);
-    int i = 0;
-    for (; i + 4 < nb; i += 4) {
-      const int k0 = i << 6;
-      load(b3, k0 + 192); compute(b0); order();
-      load(b0, k0 + 256); compute(b1); order();
-      load(b1, k0 + 320); compute(b2); order();
-      load(b2, k0 + 384); compute(b3); order();
-    }
-    load(b3, (i << 6) + 192);
-    compute(b0); compute(b1); compute(b2); compute(b3);
-  } else {
-    // Two register buffers. The loop leaves one block (nb odd) or two (nb even) in flight;
-    // a load past the last block would wrap to block `rot` and count it twice.
-    Buf b0, b1;
-    load(b0, 0);
-    int kk = 0;
-    for (; kk + 128 < kw; kk += 128) {
-      load(b1, kk + 64); compute(b0); order();
-      load(b0, kk + 128); compute(b1); order();
-    }
-    if (kk + 64 < kw) {
-      load(b1, kk + 64);
-      compute(b0);
-      compute(b1);
-    } else {
-      compute(b0);
-    }
-  }
-#pragma unroll
-  for (int f = 0; f < FB; ++f)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      red[wave][2 * f][r][lane] = acc[f][0][r];
-      red[wave][2 * f + 1][r][lane] = acc[f][1][r];
-    }
-  __syncthreads();
-  // FB x 2 x 16 x 64 outputs; block (f, tb), register r, lane l:
-  // feature n0 + 32 f + 8(r/4) + 4(l/32) + r%4, token l%32 + 32 tb.
-  // Write-out by items of one token and 8 consecutive features (16-byte loads and stores):
-  // item (m, g) covers features n0 + 8g .. +7, i.e. f = g/4, r = 4(g%4) + c%4 and
-  // l = m%32 + 32(c/4) for feature c of the item. All of an item's global loads are issued
-  // before any is used, and a thread's items are independent, so the write-out costs about
-  // one memory latency rather than one per output.
-  constexpr int ITEMS = 64 * NB / 8;
-  constexpr int IPT = (ITEMS + 64 * WAVES - 1) / (64 * WAVES);
-#pragma unroll
-  for (int it = 0; it < IPT; ++it) {
-    const int item = threadIdx.x + it * 64 * WAVES;
-    if (item >= ITEMS) break;
-    const int m = item / (NB / 8), g = item % (NB / 8);
-    const int f = g >> 2, q = g & 3, tb = m >> 5;
-    const int n = n0 + 8 * g;
-    if (m >= M || n >= N) continue;
-    float v[8];
+// in_proj: features < d_inner are x (conv-state shift, conv, SiLU), the rest z. d_inner % 64 == 0,
+// so an item is entirely x or entirely z.
+__device__ __forceinline__ void dec_inproj_item(const DecEpiArgs& e, int m, int n, const float v[8],
+                                                const bf16x8 s3[3], const bf16x8 w4[4],
+                                                const bf16x8 b8) {
+  const int di = e.d_inner;
+  if (n < di) {
+    const int64_t row = e.rows ? (int64_t)e.rows[m] : (int64_t)m;
+    bf16x8* st = reinterpret_cast<bf16x8*>(e.conv_state + (row * di + n) * 3);   // 48 bytes
+    bf16x8 xo, so[3];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int r = 4 * q + (c & 3), l = (m & 31) + 32 * (c >> 2);
-      float a = 0.0f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) a += red[w][2 * f + tb][r][l];
-      v[c] = a;
+      // state of feature n + c: elements 3c .. 3c+2 of the 24 (oldest first);
+      // taps of feature n + c: elements 4c .. 4c+3 of the 32
+      const float h0 = to_f32(s3[(3 * c) >> 3][(3 * c) & 7]);
+      const float h1 = to_f32(s3[(3 * c + 1) >> 3][(3 * c + 1) & 7]);
+      const float h2 = to_f32(s3[(3 * c + 2) >> 3][(3 * c + 2) & 7]);
+      const bf16 xb = from_f32<bf16>(v[c]);
+      float acc = e.conv_b ? to_f32(b8[c]) : 0.0f;
+      acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1)]), h0, acc);
+      acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 1]), h1, acc);
+      acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 2]), h2, acc);
+      acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 3]), to_f32(xb), acc);
+      xo[c] = from_f32<bf16>(silu(acc));
+      so[(3 * c) >> 3][(3 * c) & 7] = s3[(3 * c + 1) >> 3][(3 * c + 1) & 7];
+      so[(3 * c + 1) >> 3][(3 * c + 1) & 7] = s3[(3 * c + 2) >> 3][(3 * c + 2) & 7];
+      so[(3 * c + 2) >> 3][(3 * c + 2) & 7] = xb;
     }
-    const bool whole = n + 8 <= N;
-    if constexpr (EPI == DEC_STORE) {
-      if (whole) {
-        bf16x8 o;
+    *reinterpret_cast<bf16x8*>(e.xh + (int64_t)m * di + n) = xo;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(v[c]);
-        *reinterpret_cast<bf16x8*>(e.out + (int64_t)m * N + n) = o;
-      } else {
-        for (int c = 0; c < 8 && n + c < N; ++c) e.out[(int64_t)m * N + n + c] = from_f32<bf16>(v[c]);
-      }
-    } else if constexpr (EPI == DEC_PARTIAL) {
-      float* dst = e.partial + ((int64_t)split * M + m) * N + n;
-      if (whole) {
-        *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
-      } else {
-        for (int c = 0; c < 8 && n + c < N; ++c) dst[c] = v[c];
-      }
-    } else {
-      // in_proj: features < d_inner are x (conv-state shift, conv, SiLU), the rest z.
-      // d_inner % 64 == 0, so an item is entirely x or entirely z.
-      const int di = e.d_inner;
-      if (n < di) {
-        const int64_t row = e.rows ? (int64_t)e.rows[m] : (int64_t)m;
-        bf16x8* st = reinterpret_cast<bf16x8*>(e.conv_state + (row * di + n) * 3);   // 48 bytes
-        const bf16x8* cw = reinterpret_cast<const bf16x8*>(e.conv_w + (int64_t)n * 4);  // 64 bytes
-        bf16x8 s3[3], w4[4], b8;
+    for (int k = 0; k < 3; ++k) st[k] = so[k];
+  } else {
+    bf16x8 o;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) s3[k] = st[k];
+    for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(v[c]);
+    *reinterpret_cast<bf16x8*>(e.z + (int64_t)m * di + (n - di)) = o;
+  }
+}
+
+// ---- LDS-staged decode GEMM ------------------------------------------------------------------
+// Y[m, n] = sum_k U[m, k] W[n, k] for M <= 64 token rows: 64 output features per workgroup, K
+// split over grid.y. Both operands reach LDS through direct-to-LDS buffer loads, each
+// instruction fetching 8 whole 128-byte row segments: loads straight into the MFMA operand
+// layout touch 32 lines per instruction and 32 bytes of each, and counters showed the address
+// unit stalled on the L1 for most of such a kernel. Stages of 64 K columns (16 KB: 64 weight
+// rows and 64 token rows) rotate through 8 LDS buffers, 7 in flight while one is read; each
+// wave issues a quarter of every stage's loads. Wave w owns the 32 x 32 output tile of features
+// 32 (w & 1) and tokens 32 (w >> 1) over the whole K range, so no partial sums cross waves.
+constexpr int DL_BK = 64;                       // K columns per stage
+constexpr int DL_TILE = 64 * DL_BK * 2;         // bytes of one operand's stage tile (8 KB)
+constexpr int DL_STAGE = 2 * DL_TILE;           // weight tile, then token tile
+constexpr int DL_OUT_PITCH = 68;                // floats per token row of the output tile in LDS
+constexpr int kBufWord3 = 0x00020000;           // raw buffer descriptor word 3 (32-bit data)
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Position of 16-byte chunk c of row r inside a 128-byte LDS row: the 16 rows one LDS read
+// serves together then fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int dl_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int CNT>
+__device__ __forceinline__ void dl_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
+}
+
+template <int EPI, int DL_NBUF>   // DL_NBUF LDS stage buffers of DL_STAGE bytes
+__global__ __launch_bounds__(256)
+void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int M, int N,
+                         int K, int k_per_split, DecEpiArgs e) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 64;
+  const int split = blockIdx.y;
+  const int kbeg = split * k_per_split;
+  const int nst = k_per_split / DL_BK;
+
+  // Write-out items (token m, features n .. n+7): 512 per workgroup, two per thread. The in_proj
+  // epilogue's operands are requested first, so they arrive under the K loop.
+  constexpr int IPT = 2;
+  int it_m[IPT], it_n[IPT];
+  bf16x8 s3[IPT][3], w4[IPT][4], b8[IPT];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w4[k] = cw[k];
-        if (e.conv_b) b8 = *reinterpret_cast<const bf16x8*>(e.conv_b + n);
-        bf16x8 xo, so[3];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          // state of feature n + c: elements 3c .. 3c+2 of the 24 (oldest first);
-          // taps of feature n + c: elements 4c .. 4c+3 of the 32
-          const float h0 = to_f32(s3[(3 * c) >> 3][(3 * c) & 7]);
-          const float h1 = to_f32(s3[(3 * c + 1) >> 3][(3 * c + 1) & 7]);
-          const float h2 = to_f32(s3[(3 * c + 2) >> 3][(3 * c + 2) & 7]);
-          const bf16 xb = from_f32<bf16>(v[c]);
-          float acc = e.conv_b ? to_f32(b8[c]) : 0.0f;
-          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1)]), h0, acc);
-          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 1]), h1, acc);
-          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 2]), h2, acc);
-          acc = fmaf(to_f32(w4[c >> 1][4 * (c & 1) + 3]), to_f32(xb), acc);
-          xo[c] = from_f32<bf16>(silu(acc));
-          so[(3 * c) >> 3][(3 * c) & 7] = s3[(3 * c + 1) >> 3][(3 * c + 1) & 7];
-          so[(3 * c + 1) >> 3][(3 * c + 1) & 7] = s3[(3 * c + 2) >> 3][(3 * c + 2) & 7];
-          so[(3 * c + 2) >> 3][(3 * c + 2) & 7] = xb;
-        }
-        *reinterpret_cast<bf16x8*>(e.xh + (int64_t)m * di + n) = xo;
-#pragma unroll
-        for (int k = 0; k < 3; ++k) st[k] = so[k];
-      } else {
-        bf16x8 o;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(v[c]);
-        *reinterpret_cast<bf16x8*>(e.z + (int64_t)m * di + (n - di)) = o;
-      }
+  for (int it = 0; it < IPT; ++it) {
+    const int item = threadIdx.x + 256 * it;
+    it_m[it] = item >> 3;
+    it_n[it] = n0 + 8 * (item & 7);
+    if constexpr (EPI == DEC_INPROJ_CONV) {
+      if (it_m[it] < M && it_n[it] < N) dec_inproj_load(e, it_m[it], it_n[it], s3[it], w4[it], b8[it]);
     }
+  }
+
+  // Loads: wave w fills rows 16w .. 16w+15 of both stage tiles, 8 rows per instruction; lane l
+  // writes LDS slot l of its instruction (row +l/8, chunk position l%8) and so loads the global
+  // chunk that the swizzle puts there. Rows past N (weights) or M (tokens) repeat the last row;
+  // their results are never stored. Buffer loads: a descriptor per operand, 32-bit lane offsets,
+  // the K advance in the scalar offset.
+  uint32_t woff[2], uoff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ dl_swz(r);
+    const int wr = n0 + r < N ? r : N - 1 - n0;
+    const int ur = r < M ? r : M - 1;
+    woff[i] = (uint32_t)(((int64_t)wr * K + kbeg + c * 8) * 2);
+    uoff[i] = (uint32_t)(((int64_t)ur * K + kbeg + c * 8) * 2);
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * K), (short)0, 0x7fffffff, kBufWord3);
+  const __amdgpu_buffer_rsrc_t urs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)U, (short)0, 0x7fffffff, kBufWord3);
+#endif
+  auto issue = [&](int t, int b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    char* base = smem + b * DL_STAGE;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void_t*)(base + (2 * wave + i) * 1024), 16,
+                                               woff[i], t * DL_BK * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(urs,
+                                               (lds_void_t*)(base + DL_TILE + (2 * wave + i) * 1024),
+                                               16, uoff[i], t * DL_BK * 2, 0, 0);
+    }
+#endif
+  };
+
+  // Fragments: the A operand is the wave's 32 weight rows, B its 32 token rows; k step j of a
+  // stage takes chunk 2j + (lane / 32) of each row. Both row sets start at multiples of 32, so
+  // one swizzle serves both.
+  const int sw = dl_swz(lane & 31);
+  const int offA = (32 * (wave & 1) + (lane & 31)) * 128;
+  const int offB = DL_TILE + (32 * (wave >> 1) + (lane & 31)) * 128;
+  const int half = lane >> 5;
+  f32x16 acc0, acc1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) { acc0[r] = 0.0f; acc1[r] = 0.0f; }
+  auto compute = [&](int b) {   // all of a stage's fragment reads, then its four MFMAs
+    const char* base = smem + b * DL_STAGE;
+    bf16x8 a[4], bb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int pos = ((2 * j + half) ^ sw) << 4;
+      a[j] = *reinterpret_cast<const bf16x8*>(base + offA + pos);
+      bb[j] = *reinterpret_cast<const bf16x8*>(base + offB + pos);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], bb[j], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j + 1], bb[j + 1], acc1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the 8 LDS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // then the 4 MFMAs
+  };
+
+  const int pre = nst < DL_NBUF - 1 ? nst : DL_NBUF - 1;
+  for (int t = 0; t < pre; ++t) issue(t, t);
+  int t = 0;
+  // Steady state: stages t .. t+6 in flight (4 loads each per wave); once stage t has landed for
+  // every wave (wait, barrier), buffer t-1 is free and stage t+7 goes there.
+  for (; t + DL_NBUF - 1 < nst; ++t) {
+    dl_wait_vmcnt<4 * (DL_NBUF - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue(t + DL_NBUF - 1, (t + DL_NBUF - 1) % DL_NBUF);
+    compute(t % DL_NBUF);
+  }
+  dl_wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  for (; t < nst; ++t) compute(t % DL_NBUF);
+
+  // Output tile through LDS (token-major, fp32), then written out by items.
+  __syncthreads();
+  float* ot = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int f = 32 * (wave & 1) + 8 * (r >> 2) + 4 * half + (r & 3);
+    const int m = 32 * (wave >> 1) + (lane & 31);
+    ot[m * DL_OUT_PITCH + f] = acc0[r] + acc1[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < IPT; ++it) {
+    const int m = it_m[it], n = it_n[it];
+    if (m >= M || n >= N) continue;
+    const float4* src = reinterpret_cast<const float4*>(ot + m * DL_OUT_PITCH + (n - n0));
+    const float4 lo = src[0], hi = src[1];
+    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    if constexpr (EPI == DEC_INPROJ_CONV)
+      dec_inproj_item(e, m, n, v, s3[it], w4[it], b8[it]);
+    else
+      dec_store_item<EPI>(e, m, n, N, M, split, v);
   }
 }
 
@@ -308,154 +333,204 @@ void dec_xproj_reduce_kernel(const float* __restrict__ partial, int splits, int 
   }
 }
 
-// dt_proj (MFMA) + softplus + state update + D skip + gate for 32 channels x 16 tokens
-// (grid.y takes the token quarters of a 64-row tile, so a 64-row step runs 4 d_inner/32
-// workgroups: twice as many as with 32-token tiles, 22.6 -> 21.0 us at batch 64, as the
-// state reads of some workgroups overlap the state writes of others). Wave w computes a
-// 32x32 dt tile over the w-th quarter of dt_rank (columns past the tile's 16 tokens are
-// dropped); the four partial tiles are added in LDS. In the update, lane l takes channel
-// l % 32 and its tokens one at a time, with their 16 states in registers (every state row
-// of the thread's tokens requested before the dt_proj MFMAs).
-constexpr int UPD_CH = 32;
-constexpr int UPD_MT = 16;
-// KQ: each wave's share of dt_rank when known at compile time (0: dt_rank / 4 at run time)
-template <int KQ>
+constexpr int UPD_CH = 32;   // channels per update workgroup
+constexpr int UPD_MT = 16;   // tokens per update workgroup
+
+// Decode update, LDS-staged (dt_rank R = 128 or 256): the same 32 channels x 16 tokens per
+// workgroup and the same arithmetic as dec_update_kernel, laid out for whole-line memory access.
+// The W_dt rows of the block's channels and the delta rows of its tokens come in through
+// direct-to-LDS loads (1 KB of whole rows per instruction; 16-byte chunk c of row r kept at
+// position c ^ (r & 15), so the 16 rows an MFMA fragment read serves together hit distinct
+// bank groups); wave w sums the w-th quarter of dt_rank on MFMA from there. In the update a
+// lane owns four states of one channel (lane = channel (l / 4) of the wave's 16, quad l % 4)
+// for 8 tokens, so each state load or store instruction of a wave covers 1 KB of contiguous
+// state (16 channels x 64 bytes); y is summed over a channel's 4 lanes with lane exchanges.
+template <int R>
 __global__ __launch_bounds__(256)
-void dec_update_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
-                       const bf16* __restrict__ delta, const float* __restrict__ Bm,
-                       const float* __restrict__ Cm, const bf16* __restrict__ W_dt,
-                       const float* __restrict__ b_dt, const float* __restrict__ A_log,
-                       const float* __restrict__ Dv, float* __restrict__ state,
-                       const int32_t* __restrict__ rows, bf16* __restrict__ g, int M,
-                       int d_inner, int R) {
+__attribute__((amdgpu_waves_per_eu(4, 4)))   // 4 workgroups per CU: all 1024 of a 64-row step at once
+void dec_update_lds_kernel(const bf16* __restrict__ xh, const bf16* __restrict__ z,
+                           const bf16* __restrict__ delta, const float* __restrict__ Bm,
+                           const float* __restrict__ Cm, const bf16* __restrict__ W_dt,
+                           const float* __restrict__ b_dt, const float* __restrict__ A_log,
+                           const float* __restrict__ Dv, float* __restrict__ state,
+                           const int32_t* __restrict__ rows, bf16* __restrict__ g, int M,
+                           int d_inner) {
+  static_assert(R == 128 || R == 256, "dt_rank tile");
+  constexpr int CPR = R / 8;                  // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;               // rows per 1 KB load instruction
+  constexpr int WI = UPD_CH / RPI;            // load instructions for the W_dt tile
+  constexpr int DI = UPD_MT / RPI;            // and for the delta tile
+  __shared__ __attribute__((aligned(1024))) bf16 sW[UPD_CH * R];
+  __shared__ __attribute__((aligned(1024))) bf16 sD[UPD_MT * R];
   __shared__ float sdt[4][UPD_MT][UPD_CH + 1];
-  __shared__ float4 sbc[UPD_MT][8];         // B_t (4 float4) | C_t (4 float4) of the tile's tokens
+  __shared__ float4 sbc[UPD_MT][8];           // B_t (4 float4) | C_t (4 float4)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // provably uniform
   const int d0 = blockIdx.x * UPD_CH;
   const int m0 = blockIdx.y * UPD_MT;
   const int mend = min(M - m0, UPD_MT);
-  const int c = lane & (UPD_CH - 1);
-  const int d = d0 + c;
-  // Everything that does not depend on dt_proj is requested first, so its latency overlaps
-  // the dt_proj MFMAs and the barrier: B|C of the tile's tokens (staged into LDS after the
-  // MFMAs), A, D, the bias, the state rows and then every state row, x and z of this thread's
-  // tokens (ml0, ml0 + 8, ...). A token past the batch reads token m0's rows instead and its
-  // results are dropped. State rows of a batch are distinct: the host rejects a slot that
-  // appears twice, and without a slot map row m is token m.
+
+  // Small operands first: B|C of the tile's tokens, this lane's four A values, D and the bias of
+  // its channel, and the state rows of its 8 tokens (slot map); all L2 hits, waited for at once.
   const int t_bc = threadIdx.x >> 3, part = threadIdx.x & 7;
   float4 bcv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   if (t_bc < mend)
     bcv = *reinterpret_cast<const float4*>((part < 4 ? Bm : Cm) + (int64_t)(m0 + t_bc) * NS +
                                            4 * (part & 3));
-  float a2[NS];
-#pragma unroll
-  for (int n = 0; n < NS; ++n) a2[n] = A_log[(int64_t)d * NS + n];
+  const int cl = 16 * (wave & 1) + (lane >> 2);   // channel within the block
+  const int d = d0 + cl;
+  const int sq = lane & 3;                        // states 4 sq .. 4 sq + 3
+  const float4 al = *reinterpret_cast<const float4*>(A_log + (int64_t)d * NS + 4 * sq);
   const float Dd = Dv[d];
   const float bias = b_dt[d];
-  constexpr int TPT = UPD_MT / 8;           // tokens per thread
-  const int ml0 = (wave << 1) | (lane >> 5);
-  int64_t srow[TPT];
+  constexpr int TPT = UPD_MT / 2;                 // tokens per lane: (wave >> 1) + 2j
+  int32_t srow[TPT];
 #pragma unroll
   for (int j = 0; j < TPT; ++j) {
-    const int m = ml0 + 8 * j < mend ? m0 + ml0 + 8 * j : m0;
-    srow[j] = rows ? (int64_t)rows[m] : (int64_t)m;
+    const int ml = (wave >> 1) + 2 * j;
+    const int m = m0 + (ml < mend ? ml : 0);
+    srow[j] = rows ? rows[m] : m;
   }
+  dl_wait_vmcnt<0>();
+  // Then the W_dt and delta tiles (rows past the batch repeat the tile's first token; unused),
+  // and right behind them the state, x and z of this lane's 8 tokens (a token past the batch
+  // reads the tile's first token; its results are dropped): 24 loads, so waiting until at most
+  // 24 loads are outstanding waits for the tiles alone and leaves the state in flight under the
+  // dt_proj MFMAs. Compiler memory barriers keep the two groups in this order.
+  constexpr int NDMA = (UPD_CH + UPD_MT) / RPI / 4;   // tile load instructions per wave
+  static_assert((WI + DI) % 4 == 0, "tile loads split evenly over the waves");
+#if defined(__HIP_DEVICE_COMPILE__)
   {
-    // dt_proj on MFMA: this wave sums a quarter of dt_rank; all its fragments are fetched
-    // before the first MFMA (dt_rank <= 256 here: at most 4 k-steps per wave)
-    const int lrow = lane & 31, half = lane >> 5;
-    const int tok = m0 + lrow;              // rows >= M read row 0; their results are unused
-    const int kq = KQ ? KQ : R / 4;          // this wave's share of dt_rank (multiple of 32)
-    const bf16* dp = delta + (int64_t)(tok < M ? tok : 0) * R + wave * kq + 8 * half;
-    const bf16* wp = W_dt + (int64_t)(d0 + lrow) * R + wave * kq + 8 * half;
-    f32x16 acc;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W_dt + (int64_t)d0 * R), (short)0, 0x7fffffff, kBufWord3);
+    const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(delta + (int64_t)m0 * R), (short)0, 0x7fffffff, kBufWord3);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-    for (int kk = 0; kk < kq; kk += 64) {
-      bf16x8 a[4], w[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int k = kk + 16 * u < kq ? kk + 16 * u : kk;   // past kq: a repeat, not used
-        a[u] = *reinterpret_cast<const bf16x8*>(dp + k);
-        w[u] = *reinterpret_cast<const bf16x8*>(wp + k);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (kk + 16 * u < kq) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[u], a[u], acc, 0, 0, 0);
-    }
-    // acc row = channel, column = token
-    if (lrow < UPD_MT) {   // the MFMA's 32 token columns cover this tile's UPD_MT tokens
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sdt[wave][lrow][8 * (r >> 2) + 4 * half + (r & 3)] = acc[r];
+    for (int i = 0; i < NDMA; ++i) {
+      const int q = wave + 4 * i;
+      const bool isw = q < WI;
+      const int qq = isw ? q : q - WI;
+      const int r = RPI * qq + lane / CPR;
+      const int c = (lane % CPR) ^ (r & 15);
+      const int rr = isw ? r : (r < mend ? r : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          isw ? wrs : drs, (lds_void_t*)((isw ? (char*)sW : (char*)sD) + qq * 1024), 16,
+          (uint32_t)((rr * R + c * 8) * 2), 0, 0, 0);
     }
   }
-  float h[TPT][NS], xv[TPT], zv[TPT];
+#endif
+  asm volatile("" ::: "memory");
+  float h[TPT][4], xv[TPT], zv[TPT];
 #pragma unroll
   for (int j = 0; j < TPT; ++j) {
-    const int m = ml0 + 8 * j < mend ? m0 + ml0 + 8 * j : m0;
+    const int ml = (wave >> 1) + 2 * j;
+    const int m = m0 + (ml < mend ? ml : 0);
     const int64_t o = (int64_t)m * d_inner + d;
     xv[j] = to_f32(xh[o]);
     zv[j] = to_f32(z[o]);
-    const float4* st = reinterpret_cast<const float4*>(state + (srow[j] * d_inner + d) * NS);
+    const float4 f = *reinterpret_cast<const float4*>(state + ((int64_t)srow[j] * d_inner + d) * NS +
+                                                      4 * sq);
+    h[j][0] = f.x; h[j][1] = f.y; h[j][2] = f.z; h[j][3] = f.w;
+  }
+  dl_wait_vmcnt<3 * TPT>();
+  __builtin_amdgcn_s_barrier();                   // every wave's tile loads have landed
+  if (t_bc < mend) sbc[t_bc][part] = bcv;
+  // dt_proj: wave w sums k in [w R/4, (w+1) R/4) over the block's 32 channels (MFMA A rows)
+  // and its tokens (B columns; 16 valid, columns 16..31 repeat them and are dropped)
+  {
+    const int lr = lane & 31, hf = lane >> 5;
+    f32x16 acc;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 f = st[q];
-      h[j][4 * q] = f.x; h[j][4 * q + 1] = f.y; h[j][4 * q + 2] = f.z; h[j][4 * q + 3] = f.w;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < R / 64; ++s) {
+      const int c = (R / 32) * wave + 2 * s + hf;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(sW + lr * R + ((c ^ (lr & 15)) << 3));
+      const int tr = lr & 15;
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(sD + tr * R + ((c ^ tr) << 3));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    if (lr < UPD_MT) {   // acc row = channel, column = token
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sdt[wave][lr][8 * (r >> 2) + 4 * hf + (r & 3)] = acc[r];
     }
   }
-  if (t_bc < mend) sbc[t_bc][part] = bcv;
-  __syncthreads();
-#pragma unroll
-  for (int n = 0; n < NS; ++n) a2[n] = -fast_exp(a2[n]) * kLog2e;
+  // sdt and sbc written by every wave (LDS writes done; the state loads stay in flight)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  float a2[4] = {-fast_exp(al.x) * kLog2e, -fast_exp(al.y) * kLog2e, -fast_exp(al.z) * kLog2e,
+                 -fast_exp(al.w) * kLog2e};
+  // All of the lane's tokens are updated first, then y is summed over each channel's 4 lanes
+  // (DPP quad exchanges: partners 1 apart, then 2 apart; every lane of the quad ends with the
+  // same sum, in a fixed order), then one lane per channel writes g.
+  float yp[TPT];
 #pragma unroll
   for (int j = 0; j < TPT; ++j) {
-    const int ml = ml0 + 8 * j;
-    if (ml < mend) {
-      const int m = m0 + ml;
-      const int64_t o = (int64_t)m * d_inner + d;
-      const float dtv =
-          softplus(((sdt[0][ml][c] + sdt[1][ml][c]) + (sdt[2][ml][c] + sdt[3][ml][c])) + bias);
-      const float dx = dtv * xv[j];
-      float bb[NS], cc[NS];
+    const int ml = (wave >> 1) + 2 * j;
+    const int mc = ml < mend ? ml : 0;           // tokens past the batch: computed, not stored
+    const float dtv = softplus(((sdt[0][mc][cl] + sdt[1][mc][cl]) +
+                                (sdt[2][mc][cl] + sdt[3][mc][cl])) + bias);
+    const float dx = dtv * xv[j];
+    const float4 b4 = sbc[mc][sq], c4 = sbc[mc][4 + sq];
+    const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, cc[4] = {c4.x, c4.y, c4.z, c4.w};
+    float acc = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 b4 = sbc[ml][q], c4 = sbc[ml][4 + q];
-        bb[4 * q] = b4.x; bb[4 * q + 1] = b4.y; bb[4 * q + 2] = b4.z; bb[4 * q + 3] = b4.w;
-        cc[4 * q] = c4.x; cc[4 * q + 1] = c4.y; cc[4 * q + 2] = c4.z; cc[4 * q + 3] = c4.w;
-      }
-      float y = 0.0f;
+    for (int k = 0; k < 4; ++k) {
+      h[j][k] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[k]), h[j][k], dx * bb[k]);
+      acc = fmaf(cc[k], h[j][k], acc);
+    }
+    yp[j] = acc;
+    if (ml < mend)
+      *reinterpret_cast<float4*>(state + ((int64_t)srow[j] * d_inner + d) * NS + 4 * sq) =
+          make_float4(h[j][0], h[j][1], h[j][2], h[j][3]);
+  }
 #pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        h[j][n] = fmaf(__builtin_amdgcn_exp2f(dtv * a2[n]), h[j][n], dx * bb[n]);
-        y = fmaf(cc[n], h[j][n], y);
-      }
-      float4* st = reinterpret_cast<float4*>(state + (srow[j] * d_inner + d) * NS);
+  for (int j = 0; j < TPT; ++j) {
+    const float y01 = yp[j] + __int_as_float(__builtin_amdgcn_update_dpp(
+                                  0, __float_as_int(yp[j]), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    yp[j] = y01 + __int_as_float(__builtin_amdgcn_update_dpp(
+                      0, __float_as_int(y01), 0x4E, 0xF, 0xF, false));                  // quad [2,3,0,1]
+  }
+  if (sq == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        st[q] = make_float4(h[j][4 * q], h[j][4 * q + 1], h[j][4 * q + 2], h[j][4 * q + 3]);
-      y = fmaf(Dd, xv[j], y);
-      g[o] = from_f32<bf16>(y * silu(zv[j]));
+    for (int j = 0; j < TPT; ++j) {
+      const int ml = (wave >> 1) + 2 * j;
+      if (ml < mend)
+        g[(int64_t)(m0 + ml) * d_inner + d] = from_f32<bf16>(fmaf(Dd, xv[j], yp[j]) * silu(zv[j]));
     }
   }
 }
 
-template <int WAVES, int FB, int EPI>
-hipError_t launch_dec_gemm(const bf16* U, const bf16* W, int M, int N, int K, int splits,
-                           const DecEpiArgs& e, hipStream_t s) {
-  dim3 grid((N + 32 * FB - 1) / (32 * FB), splits);
-  hipLaunchKernelGGL((dec_gemm_kernel<WAVES, FB, EPI>), grid, dim3(64 * WAVES), 0, s, U, W, M, N,
-                     K, K / splits, e);
+// Dynamic LDS above 64 KB is enabled once per device (per-device flags, thread-safe).
+constexpr int kDlMaxDevices = 64;
+template <int EPI, int NBUF = 8>
+hipError_t launch_dec_gemm_lds(const bf16* U, const bf16* W, int M, int N, int K, int splits,
+                               const DecEpiArgs& e, hipStream_t s) {
+  constexpr int DL_LDS = NBUF * DL_STAGE;
+  static std::atomic<bool> lds_set[kDlMaxDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kDlMaxDevices) return hipErrorInvalidDevice;
+  if (!lds_set[dev].load(std::memory_order_acquire)) {
+    err = hipFuncSetAttribute((const void*)dec_gemm_lds_kernel<EPI, NBUF>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, DL_LDS);
+    if (err != hipSuccess) return err;
+    lds_set[dev].store(true, std::memory_order_release);
+  }
+  dim3 grid((N + 63) / 64, splits);
+  hipLaunchKernelGGL((dec_gemm_lds_kernel<EPI, NBUF>), grid, dim3(256), DL_LDS, s, U, W, M, N, K,
+                     K / splits, e);
   return hipGetLastError();
 }
 
-constexpr int XPROJ_SPLIT_K = 512;   // K per workgroup for x_proj
-constexpr int OUTPROJ_SPLITS = 4;
+constexpr int XPROJ_SPLIT_K = 512;   // K per workgroup for x_proj (16 splits at d_inner 8192)
+constexpr int OUTPROJ_SPLITS = 4;   // out_proj split-K (256 workgroups at d_model 4096)
 
 }  // namespace
 
 bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank) {
-  return d_model % 256 == 0 && d_inner % 1024 == 0 && dt_rank % 128 == 0;
+  return d_model % 256 == 0 && d_inner % 1024 == 0 && (dt_rank == 128 || dt_rank == 256);
 }
 
 size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile) {
@@ -471,7 +546,7 @@ hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_
   e.xh = xh; e.z = z; e.conv_state = conv_state; e.rows = rows; e.conv_w = conv_w;
   e.conv_b = conv_b;
   e.d_inner = d_inner;
-  return launch_dec_gemm<4, 2, DEC_INPROJ_CONV>(u, W_in, M, 2 * d_inner, d_model, 1, e, s);
+  return launch_dec_gemm_lds<DEC_INPROJ_CONV>(u, W_in, M, 2 * d_inner, d_model, 1, e, s);
 }
 
 hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf16* delta,
@@ -481,7 +556,7 @@ hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf
   const int splits = d_inner / XPROJ_SPLIT_K;   // 128-deep K slice per wave
   DecEpiArgs e = {};
   e.partial = partial;
-  hipError_t err = launch_dec_gemm<4, 1, DEC_PARTIAL>(xh, W_x, M, N, d_inner, splits, e, s);
+  hipError_t err = launch_dec_gemm_lds<DEC_PARTIAL>(xh, W_x, M, N, d_inner, splits, e, s);
   if (err != hipSuccess) return err;
   const dim3 rgrid((M * (N / 4) + 255) / 256);
   if (splits == 16)   // d_inner 8192
@@ -500,14 +575,11 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
                              hipStream_t s) {
   const dim3 grid(d_inner / UPD_CH, (M + UPD_MT - 1) / UPD_MT);
   if (dt_rank == 256)
-    hipLaunchKernelGGL(dec_update_kernel<64>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
-                       b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
-  else if (dt_rank == 128)
-    hipLaunchKernelGGL(dec_update_kernel<32>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
-                       b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
-  else
-    hipLaunchKernelGGL(dec_update_kernel<0>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm, W_dt,
-                       b_dt, A_log, D, ssm_state, rows, g, M, d_inner, dt_rank);
+    hipLaunchKernelGGL(dec_update_lds_kernel<256>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm,
+                       W_dt, b_dt, A_log, D, ssm_state, rows, g, M, d_inner);
+  else   // dt_rank 128 (decode_fast_path_ok)
+    hipLaunchKernelGGL(dec_update_lds_kernel<128>, grid, dim3(256), 0, s, xh, z, delta, Bm, Cm,
+                       W_dt, b_dt, A_log, D, ssm_state, rows, g, M, d_inner);
   return hipGetLastError();
 }
 
@@ -515,8 +587,8 @@ hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial,
                                int d_model, int d_inner, hipStream_t s) {
   DecEpiArgs e = {};
   e.partial = partial;
-  hipError_t err = launch_dec_gemm<4, 2, DEC_PARTIAL>(g, W_out, M, d_model, d_inner,
-                                                      OUTPROJ_SPLITS, e, s);
+  hipError_t err = launch_dec_gemm_lds<DEC_PARTIAL>(g, W_out, M, d_model, d_inner,
+                                                   OUTPROJ_SPLITS, e, s);
   if (err != hipSuccess) return err;
   const int64_t count = (int64_t)M * d_model;
   hipLaunchKernelGGL(dec_sum_partials_kernel<OUTPROJ_SPLITS>,

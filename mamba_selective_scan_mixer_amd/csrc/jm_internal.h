@@ -149,7 +149,7 @@ hipError_t launch_inner_rmsnorm(T* delta, float* Bm, float* Cm, const float* g_d
                                 const float* g_B, const float* g_C, float eps, int64_t M, int R,
                                 hipStream_t s);
 
-// Decode fast path (bf16; d_model % 256, d_inner % 1024, dt_rank % 128; <= 64 rows per launch).
+// Decode fast path (bf16; d_model % 256, d_inner % 1024, dt_rank 128 or 256; <= 64 rows per launch).
 bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank);
 size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile);
 // rows: state row (slot) of each token row, or NULL for row m = token row m.

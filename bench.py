@@ -28,7 +28,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 # fp32 VALU issue rate without packed math: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
-# issue slots per SSM state update: mul, exp2 (~2 slots on gfx950), mul, fma (+ fma for y)
+# issue slots per SSM state update when no counter record applies (a model: mul, exp2, mul, fma,
+# + fma for y; the exp counted as two slots)
 SCAN_SLOTS = {"scan_chunk_state": 5.0, "scan_chunk_output": 6.0}
 METRIC = "Mamba-layer prefill tok/s @128K, decode tok/s @B=64; % HBM/MFMA peak"
 
@@ -78,6 +79,31 @@ def recorded_traffic(kernel: str):
             return None
         return (float(rec["fetch_kib"]) * float(rec["fetch_factor"])
                 + float(rec["write_kib"]) * float(rec["write_factor"])) * 1024.0
+    except OSError:
+        return None
+
+
+def recorded_valu(kernel: str):
+    """Measured wave-level VALU instructions per lane state update of a scan kernel, from the
+    committed rocprofv3 counter summary (SQ_INSTS_VALU x 64 / updates), or None when the scan
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_128k_mfma_valu_counters.md")
+    srcs = [os.path.join(ROOT, "mamba_selective_scan_mixer_amd", "csrc", f)
+            for f in ("jm_scan.hip", "jm_internal.h")]
+    try:
+        rec = None
+        for line in open(path):
+            if line.startswith("valu-record:"):
+                kv = dict(t.split("=", 1) for t in line.split()[1:])
+                if kv.get("kernel") == kernel:
+                    rec = kv
+        if rec is None:
+            return None
+        h = hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest()[:16]
+        if h != rec["source_sha256"]:
+            return None
+        return float(rec["valu_insts_per_update"])
     except OSError:
         return None
 
@@ -218,7 +244,13 @@ def main():
                 updates = float(T) * d.d_inner * 16
                 if name == "scan_chunk_state":
                     updates *= (nc - 1) / nc      # the last chunk needs no aggregate
-                k["alu_frac"] = round(updates * SCAN_SLOTS[name] / VALU_LANE_OPS / (avg * 1e-3), 4)
+                per = recorded_valu(name)
+                k["alu_basis"] = ("measured VALU instructions per update (rocprofv3 SQ_INSTS_VALU, "
+                                  "profiles/prefill_128k_mfma_valu_counters.md)" if per is not None
+                                  else "slot model")
+                per = SCAN_SLOTS[name] if per is None else per
+                k["valu_per_update"] = per
+                k["alu_frac"] = round(updates * per / VALU_LANE_OPS / (avg * 1e-3), 4)
             if b == "mfma":
                 k["frac"] = round(k["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
             elif b == "alu":

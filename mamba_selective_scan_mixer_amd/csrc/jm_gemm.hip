@@ -492,20 +492,55 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
       if (nk > 1) issue_x(1, 1);
     }
     // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
-#pragma unroll
-    for (int a = 0; a < FN; ++a)
-#pragma unroll
-      for (int b = 0; b < FM; ++b) {
-        const int64_t m = em0 + wm0 + b * 32 + lrow;
-        if (m >= M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = en0 + wn0 + a * 32 + 8 * q + 4 * khalf;
-          float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                        acc[a][b][4 * q + 3]};
-          epilogue<bf16, EPI>(epi, m, n, N, v);
-        }
+    // A tile whose 256 features lie inside one output (every tile of STORE; of SPLIT2 when the
+    // split is a multiple of 256) gets its base and row stride once per tile, so its stores carry
+    // no per-lane output selection or bounds test (with one, the compiler emitted every store on
+    // both paths under execution masks: 192 store instructions instead of 64).
+    bf16* tile_out = nullptr;
+    int64_t tile_ld = 0;
+    if constexpr (EPI == EPI_STORE) {
+      if (en0 + BN <= N) {
+        tile_out = static_cast<bf16*>(epi.out0) + en0;
+        tile_ld = epi.ldo;
       }
+    } else if constexpr (EPI == EPI_SPLIT2) {
+      if (en0 + BN <= N && epi.split % BN == 0) {
+        tile_out = en0 < epi.split ? static_cast<bf16*>(epi.out0) + en0
+                                   : static_cast<bf16*>(epi.out1) + (en0 - epi.split);
+        tile_ld = epi.split;
+      }
+    }
+    if ((EPI == EPI_STORE || EPI == EPI_SPLIT2) && tile_out) {
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+          const int64_t m = em0 + wm0 + b * 32 + lrow;
+          if (m >= M) continue;
+          bf16* row = tile_out + m * tile_ld + wn0 + a * 32 + 4 * khalf;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                                acc[a][b][4 * q + 3]};
+            store4<bf16>(row + 8 * q, v, 4);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < FN; ++a)
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+          const int64_t m = em0 + wm0 + b * 32 + lrow;
+          if (m >= M) continue;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = en0 + wn0 + a * 32 + 8 * q + 4 * khalf;
+            float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
+                          acc[a][b][4 * q + 3]};
+            epilogue<bf16, EPI>(epi, m, n, N, v);
+          }
+        }
+    }
     if (next >= n_tiles) break;
     // a whole tile issued exactly NST stores, all after the loads above
     stores_pending = em0 + BM <= M && en0 + BN <= N;

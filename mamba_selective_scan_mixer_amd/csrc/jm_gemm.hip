@@ -260,9 +260,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // 256 x 256 tiles, 8 waves, K slices of 64 (128-byte row segments: one L2 request per row per
-// slice, half the requests of 64-byte segments), two LDS buffers of 64 KB.
+// slice, half the requests of 64-byte segments), two LDS buffers of 64 KB, and 4 KB per wave
+// behind them where the epilogue turns result rows into whole 128-byte lines.
 constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 4, MS_WN = 2, MS_BK = 64;
-constexpr int MS_LDS_BYTES = 2 * (MS_BM + MS_BN) * MS_BK * 2;
+constexpr int MS_EPI_WAVE_BYTES = 32 * 128;   // 32 token rows x 64 bf16 features
+constexpr int MS_LDS_BYTES =
+    2 * (MS_BM + MS_BN) * MS_BK * 2 + MS_WM * MS_WN * MS_EPI_WAVE_BYTES;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKC, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
@@ -282,6 +285,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   constexpr int NM = FN * FM;                // MFMAs per k16 step
   constexpr int NR = FN + FM;                // fragment reads per k16 step
   static_assert(BKC == 64 && SPS == 4 && XI >= 1 && WI >= 1 && NM % 2 == 0, "tiling");
+  static_assert(FN % 2 == 0, "the staged epilogue writes 64-feature row segments");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   bf16* lds = reinterpret_cast<bf16*>(smem);
 
@@ -290,6 +294,8 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   const int wave = threadIdx.x >> 6;
   const int wm0 = (wave / WAVES_N) * TM;
   const int wn0 = (wave % WAVES_N) * TN;
+  // this wave's epilogue staging area, behind the two stage buffers
+  char* const stg = smem + 2 * STAGE * 2 + wave * MS_EPI_WAVE_BYTES;
 
   // Persistent: workgroup b takes tiles b, b + G, b + 2G, ... (G = gridDim.x, a multiple of
   // 8, so a workgroup stays on one XCD and the tile order per XCD is the one tile_coords
@@ -385,18 +391,22 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // buffer; the X half of stage kt+2 goes there at once, the W half during stage kt+1's first
   // k16 step; both are waited for (vmcnt 0) before the barrier that ends stage kt+1.
   const int nk = K / BKC;
-  // stores this wave issues for a whole tile (one per epilogue call)
+  // store instructions this wave issues for a whole tile: the staged epilogue (1 KB of whole
+  // lines each) and the per-element one (one per 4 results)
+  constexpr int NST_LINES = FM * (FN / 2) * 4;
   constexpr int NST = FN * FM * 4;
   int tile = blockIdx.x;
   setup(tile);
   issue_x(0, 0);
   issue_w(0, 0);
   if (nk > 1) issue_x(1, 1);
-  bool stores_pending = false;   // the previous tile's NST stores were issued after these loads
+  int stores_pending = 0;   // store instructions of the previous tile issued after these loads
   for (;;) {
     if (nk > 1) {
       // stage 0 complete; stage 1's X half (and the previous tile's stores) may be in flight
-      if (stores_pending) wait_vmcnt<XI + NST>(); else wait_vmcnt<XI>();
+      if (stores_pending == NST) wait_vmcnt<XI + NST>();
+      else if (stores_pending == NST_LINES) wait_vmcnt<XI + NST_LINES>();
+      else wait_vmcnt<XI>();
     } else {
       wait_vmcnt<0>();
     }
@@ -493,13 +503,17 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
     }
     // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
     // A tile whose 256 features lie inside one output (every tile of STORE; of SPLIT2 when the
-    // split is a multiple of 256) gets its base and row stride once per tile, so its stores carry
-    // no per-lane output selection or bounds test (with one, the compiler emitted every store on
-    // both paths under execution masks: 192 store instructions instead of 64).
+    // split is a multiple of 256), with 16-byte aligned rows, gets its base and row stride once
+    // per tile and goes out as whole lines: per 32 tokens x 64 features, each wave writes its
+    // results into its own 4 KB of LDS (row r, 16-byte chunk c at position c ^ (r & 7), so a
+    // write or a read of 8 rows touches every bank once) and reads them back a row segment per
+    // 8 lanes, so each store instruction writes 8 whole 128-byte lines. Stored straight from the
+    // MFMA layout, each instruction wrote 16 bytes into each of 32 rows, and the L2 write
+    // requests (16 per line) took ~10% of in_proj's time.
     bf16* tile_out = nullptr;
     int64_t tile_ld = 0;
     if constexpr (EPI == EPI_STORE) {
-      if (en0 + BN <= N) {
+      if (en0 + BN <= N && epi.ldo % 8 == 0) {
         tile_out = static_cast<bf16*>(epi.out0) + en0;
         tile_ld = epi.ldo;
       }
@@ -510,19 +524,31 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
         tile_ld = epi.split;
       }
     }
+    if (tile_out && (reinterpret_cast<uintptr_t>(tile_out) & 15) != 0) tile_out = nullptr;
     if ((EPI == EPI_STORE || EPI == EPI_SPLIT2) && tile_out) {
 #pragma unroll
-      for (int a = 0; a < FN; ++a)
+      for (int b = 0; b < FM; ++b)
 #pragma unroll
-        for (int b = 0; b < FM; ++b) {
-          const int64_t m = em0 + wm0 + b * 32 + lrow;
-          if (m >= M) continue;
-          bf16* row = tile_out + m * tile_ld + wn0 + a * 32 + 4 * khalf;
+        for (int ap = 0; ap < FN / 2; ++ap) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                                acc[a][b][4 * q + 3]};
-            store4<bf16>(row + 8 * q, v, 4);
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x16& c = acc[2 * ap + j][b];
+              const bf16 h[4] = {from_f32<bf16>(c[4 * q]), from_f32<bf16>(c[4 * q + 1]),
+                                 from_f32<bf16>(c[4 * q + 2]), from_f32<bf16>(c[4 * q + 3])};
+              const int chunk = 4 * j + q;   // features 8 chunk .. 8 chunk + 7 of the 64
+              *reinterpret_cast<uint2*>(stg + lrow * 128 + ((chunk ^ (lrow & 7)) << 4) +
+                                        khalf * 8) = *reinterpret_cast<const uint2*>(h);
+            }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int rr = 8 * i + (lane >> 3), cc = lane & 7;
+            const uint4 v =
+                *reinterpret_cast<const uint4*>(stg + rr * 128 + ((cc ^ (rr & 7)) << 4));
+            const int64_t m = em0 + wm0 + b * 32 + rr;
+            if (m < M)
+              *reinterpret_cast<uint4*>(tile_out + m * tile_ld + wn0 + ap * 64 + cc * 8) = v;
           }
         }
     } else {
@@ -542,8 +568,12 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
         }
     }
     if (next >= n_tiles) break;
-    // a whole tile issued exactly NST stores, all after the loads above
-    stores_pending = em0 + BM <= M && en0 + BN <= N;
+    // A whole tile issued exactly NST_LINES (staged) or at least NST (per element: a wave whose
+    // lanes straddle two outputs issues both stores) store instructions, all after the loads
+    // above; a partial tile may skip some, so the next wait takes them all.
+    stores_pending = em0 + BM <= M && en0 + BN <= N
+                         ? ((EPI == EPI_STORE || EPI == EPI_SPLIT2) && tile_out ? NST_LINES : NST)
+                         : 0;
     tile = next;
   }
 }

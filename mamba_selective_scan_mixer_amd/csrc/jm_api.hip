@@ -202,7 +202,7 @@ PrefillLayout prefill_layout(const jm_layer_dims& d, int64_t T, int32_t n_chunks
 }
 
 struct DecodeLayout {
-  size_t x, z, xh, delta, Bm, Cm, g, partial, total;
+  size_t x, z, xh, delta, Bm, Cm, g, partial, counters, total;
 };
 
 DecodeLayout decode_layout(const jm_layer_dims& d, int64_t b) {
@@ -221,6 +221,7 @@ DecodeLayout decode_layout(const jm_layer_dims& d, int64_t b) {
   const bool fast = d.act_dtype == JM_BF16 && decode_fast_path_ok(d.d_model, d.d_inner, d.dt_rank);
   L.partial = take(fast ? decode_fast_partial_floats(d.d_model, d.d_inner, d.dt_rank, 64) * sizeof(float)
                         : 0);
+  L.counters = take(fast ? decode_fast_counters(d.d_model) * sizeof(int) : 0);
   L.total = off;
   return L;
 }
@@ -418,6 +419,7 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
   if constexpr (sizeof(T) == 2) {
     if (decode_fast_path_ok(dm, di, R)) {
       float* partial = reinterpret_cast<float*>(ws + L.partial);
+      int* counters = reinterpret_cast<int*>(ws + L.counters);
       const bf16* Win = static_cast<const bf16*>(w.in_proj_w);
       for (int32_t b0 = 0; b0 < b; b0 += 64) {
         const int M = b - b0 < 64 ? b - b0 : 64;
@@ -430,7 +432,7 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
         bf16* ot = out + (int64_t)b0 * dm;
         JM_LAUNCH("dec_in_proj", launch_dec_in_proj(ut, Win, static_cast<const bf16*>(w.conv_w),
                                                     static_cast<const bf16*>(w.conv_b), ct, rt, xh,
-                                                    z, M, dm, di, stream));
+                                                    z, counters, M, dm, di, stream));
         JM_LAUNCH("dec_x_proj", launch_dec_x_proj(xh, static_cast<const bf16*>(w.x_proj_w),
                                                   partial, delta, Bm, Cm, M, di, R, stream));
         if (w.dt_norm_w)
@@ -440,7 +442,7 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
         jm_status su = step_decode_update<bf16>(d, w, xh, z, delta, Bm, Cm, M, st, rt, g, stream);
         if (su != JM_OK) return su;
         JM_LAUNCH("dec_out_proj", launch_dec_out_proj(g, static_cast<const bf16*>(w.out_proj_w),
-                                                      partial, ot, M, dm, di, stream));
+                                                      partial, counters, ot, M, dm, di, stream));
       }
       return ok();
     }

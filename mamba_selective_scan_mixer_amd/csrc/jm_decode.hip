@@ -10,7 +10,9 @@
 //                 64 K columns in flight; each wave owns a 32 x 32 output tile.
 //   in_proj epilogue: the conv-state shift, the causal conv (kernel 4) and SiLU are
 //                 applied right there for the x half; the z half is stored.
-//   xproj_reduce, sum_partials: the split-K partial sums, added in a fixed order.
+//   out_proj epilogue: the workgroup that completes a 64-feature block last adds the four
+//                 split-K partial sums in split order and writes the bf16 output.
+//   xproj_reduce: x_proj's split-K partial sums, added in a fixed order.
 //   update        per 32 channels x 16 sequences: dt_proj on MFMA (W_dt and delta rows
 //                 staged in LDS), softplus, the 16-state update in place, the D skip and
 //                 the SiLU(z) gate.
@@ -23,7 +25,9 @@ namespace {
 
 constexpr int NS = 16;
 
-enum DecEpi : int { DEC_STORE = 0, DEC_INPROJ_CONV = 1, DEC_PARTIAL = 2 };
+enum DecEpi : int { DEC_STORE = 0, DEC_INPROJ_CONV = 1, DEC_PARTIAL = 2, DEC_PARTIAL_SUM = 3 };
+
+constexpr int OUTPROJ_SPLITS = 4;   // out_proj split-K (256 workgroups at d_model 4096)
 
 struct DecEpiArgs {
   bf16* out;             // STORE: (M, N) bf16
@@ -34,7 +38,9 @@ struct DecEpiArgs {
   const bf16* conv_w;    // INPROJ: (d_inner, 4)
   const bf16* conv_b;    // INPROJ: (d_inner) or null
   int d_inner;           // INPROJ split point
-  float* partial;        // PARTIAL: (splits, M, N) fp32
+  float* partial;        // PARTIAL: (splits, M, N) fp32; PARTIAL_SUM: per split, block, thread
+  int* counters;         // INPROJ: zeroed (n_counters); PARTIAL_SUM: arrivals per 64-feature block
+  int n_counters;
 };
 
 // ---- write-out of one item: token m, features n .. n+7 (n % 8 == 0) ------------------------
@@ -143,6 +149,76 @@ __device__ __forceinline__ void dl_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
 }
 
+// out_proj's split-K epilogue. Each workgroup stores its 64 x 64 partial sums (16 per thread, as
+// 8-byte halves at [split][block][c][thread], so a wave's store covers 512 contiguous bytes) and
+// then counts itself in for its block of 64 features; the workgroup that arrives last reads the
+// other splits back and writes bf16(0 + p0 + p1 + p2 + p3), the sum of a separate reduction
+// launch in the same order. The workgroups of a block run on different XCDs, whose L2 caches are
+// not coherent with each other: the partial sums go through agent-scope atomic stores and loads,
+// which reach the device-coherent level, and only the ordering is fenced (every store has
+// completed, vmcnt(0), before the count moves; the reads start after the count is seen), so no
+// L2 write-back or invalidation is needed.
+__device__ __forceinline__ void dec_partial_sum_epilogue(const DecEpiArgs& e, const float* ot,
+                                                         const int it_m[2], const int it_n[2],
+                                                         int n0, int M, int N, int split,
+                                                         int* last_flag) {
+  float own[16];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const float4* src = reinterpret_cast<const float4*>(ot + it_m[it] * DL_OUT_PITCH + (it_n[it] - n0));
+    const float4 lo = src[0], hi = src[1];
+    own[8 * it + 0] = lo.x; own[8 * it + 1] = lo.y; own[8 * it + 2] = lo.z; own[8 * it + 3] = lo.w;
+    own[8 * it + 4] = hi.x; own[8 * it + 5] = hi.y; own[8 * it + 6] = hi.z; own[8 * it + 7] = hi.w;
+  }
+  uint64_t* P = reinterpret_cast<uint64_t*>(e.partial);
+  const int64_t blocks = gridDim.x;
+  auto slot = [&](int s, int c) {
+    return P + ((((int64_t)s * blocks + blockIdx.x) * 8 + c) * 256 + threadIdx.x);
+  };
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint64_t w = (uint64_t)__float_as_uint(own[2 * c]) |
+                       ((uint64_t)__float_as_uint(own[2 * c + 1]) << 32);
+    __hip_atomic_store(slot(split, c), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this thread's partial sums have landed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *last_flag = __hip_atomic_fetch_add(e.counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == OUTPROJ_SPLITS - 1;
+  __syncthreads();
+  if (!*last_flag) return;
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // every split's values, this workgroup's own included (they round-trip bit-exactly)
+  uint64_t q[OUTPROJ_SPLITS][8];
+#pragma unroll
+  for (int s = 0; s < OUTPROJ_SPLITS; ++s)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      q[s][c] = __hip_atomic_load(slot(s, c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float sum[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sum[j] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < OUTPROJ_SPLITS; ++s)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      sum[2 * c] += __uint_as_float((uint32_t)q[s][c]);
+      sum[2 * c + 1] += __uint_as_float((uint32_t)(q[s][c] >> 32));
+    }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int m = it_m[it], n = it_n[it];
+    if (m >= M || n >= N) continue;
+    bf16x8 o;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = from_f32<bf16>(sum[8 * it + c]);
+    *reinterpret_cast<bf16x8*>(e.out + (int64_t)m * N + n) = o;
+  }
+}
+
 template <int EPI, int DL_NBUF>   // DL_NBUF LDS stage buffers of DL_STAGE bytes
 __global__ __launch_bounds__(256)
 void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int M, int N,
@@ -167,6 +243,11 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
     if constexpr (EPI == DEC_INPROJ_CONV) {
       if (it_m[it] < M && it_n[it] < N) dec_inproj_load(e, it_m[it], it_n[it], s3[it], w4[it], b8[it]);
     }
+  }
+  // in_proj clears the arrival counters of the out_proj launched after it in the same step
+  if constexpr (EPI == DEC_INPROJ_CONV) {
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int i = threadIdx.x; i < e.n_counters; i += 256) e.counters[i] = 0;
   }
 
   // Loads: wave w fills rows 16w .. 16w+15 of both stage tiles, 8 rows per instruction; lane l
@@ -257,6 +338,11 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
     ot[m * DL_OUT_PITCH + f] = acc0[r] + acc1[r];
   }
   __syncthreads();
+  if constexpr (EPI == DEC_PARTIAL_SUM) {
+    dec_partial_sum_epilogue(e, ot, it_m, it_n, n0, M, N, split,
+                             reinterpret_cast<int*>(smem + 64 * DL_OUT_PITCH * 4));
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < IPT; ++it) {
     const int m = it_m[it], n = it_n[it];
@@ -293,20 +379,6 @@ __device__ __forceinline__ float4 sum_splits(const float* __restrict__ p, int sp
     }
   }
   return v;
-}
-
-// out = bf16(sum of split-K partials); 4 outputs per thread (count % 4 == 0).
-template <int SPLITS>
-__global__ __launch_bounds__(256)
-void dec_sum_partials_kernel(const float* __restrict__ partial, int splits, int64_t count,
-                             bf16* __restrict__ out) {
-  const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i4 >= count) return;
-  const float4 v = sum_splits<SPLITS>(partial + i4, splits, count);
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  const bf16x4 o = {from_f32<bf16>(v.x), from_f32<bf16>(v.y), from_f32<bf16>(v.z),
-                    from_f32<bf16>(v.w)};
-  *reinterpret_cast<bf16x4*>(out + i4) = o;
 }
 
 // Sum split-K partials of x_proj: delta (bf16), B and C (fp32); 4 outputs per thread (R and
@@ -525,13 +597,14 @@ hipError_t launch_dec_gemm_lds(const bf16* U, const bf16* W, int M, int N, int K
 }
 
 constexpr int XPROJ_SPLIT_K = 512;   // K per workgroup for x_proj (16 splits at d_inner 8192)
-constexpr int OUTPROJ_SPLITS = 4;   // out_proj split-K (256 workgroups at d_model 4096)
 
 }  // namespace
 
 bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank) {
   return d_model % 256 == 0 && d_inner % 1024 == 0 && (dt_rank == 128 || dt_rank == 256);
 }
+
+int decode_fast_counters(int d_model) { return d_model / 64; }
 
 size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile) {
   const size_t xp = (size_t)(d_inner / XPROJ_SPLIT_K) * batch_tile * (dt_rank + 2 * NS);
@@ -541,10 +614,13 @@ size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int bat
 
 hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
                               const bf16* conv_b, bf16* conv_state, const int32_t* rows,
-                              bf16* xh, bf16* z, int M, int d_model, int d_inner, hipStream_t s) {
+                              bf16* xh, bf16* z, int* counters, int M, int d_model, int d_inner,
+                              hipStream_t s) {
   DecEpiArgs e = {};
   e.xh = xh; e.z = z; e.conv_state = conv_state; e.rows = rows; e.conv_w = conv_w;
   e.conv_b = conv_b;
+  e.counters = counters;
+  e.n_counters = decode_fast_counters(d_model);
   e.d_inner = d_inner;
   return launch_dec_gemm_lds<DEC_INPROJ_CONV>(u, W_in, M, 2 * d_inner, d_model, 1, e, s);
 }
@@ -583,18 +659,14 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
   return hipGetLastError();
 }
 
-hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, bf16* out, int M,
-                               int d_model, int d_inner, hipStream_t s) {
+hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, int* counters,
+                               bf16* out, int M, int d_model, int d_inner, hipStream_t s) {
   DecEpiArgs e = {};
   e.partial = partial;
-  hipError_t err = launch_dec_gemm_lds<DEC_PARTIAL>(g, W_out, M, d_model, d_inner,
-                                                   OUTPROJ_SPLITS, e, s);
-  if (err != hipSuccess) return err;
-  const int64_t count = (int64_t)M * d_model;
-  hipLaunchKernelGGL(dec_sum_partials_kernel<OUTPROJ_SPLITS>,
-                     dim3((unsigned)((count / 4 + 255) / 256)), dim3(256), 0, s, partial,
-                     OUTPROJ_SPLITS, count, out);
-  return hipGetLastError();
+  e.counters = counters;
+  e.out = out;
+  return launch_dec_gemm_lds<DEC_PARTIAL_SUM>(g, W_out, M, d_model, d_inner, OUTPROJ_SPLITS, e,
+                                              s);
 }
 
 }  // namespace jm

@@ -152,10 +152,14 @@ hipError_t launch_inner_rmsnorm(T* delta, float* Bm, float* Cm, const float* g_d
 // Decode fast path (bf16; d_model % 256, d_inner % 1024, dt_rank 128 or 256; <= 64 rows per launch).
 bool decode_fast_path_ok(int d_model, int d_inner, int dt_rank);
 size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int batch_tile);
-// rows: state row (slot) of each token row, or NULL for row m = token row m.
+// Arrival counters out_proj needs (one per 64 output features); in_proj zeroes them.
+int decode_fast_counters(int d_model);
+// rows: state row (slot) of each token row, or NULL for row m = token row m. counters:
+// decode_fast_counters(d_model) ints that in_proj sets to zero for the out_proj that follows.
 hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
                               const bf16* conv_b, bf16* conv_state, const int32_t* rows,
-                              bf16* xh, bf16* z, int M, int d_model, int d_inner, hipStream_t s);
+                              bf16* xh, bf16* z, int* counters, int M, int d_model, int d_inner,
+                              hipStream_t s);
 hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf16* delta,
                              float* Bm, float* Cm, int M, int d_inner, int dt_rank, hipStream_t s);
 hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, const float* Bm,
@@ -163,7 +167,8 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
                              const float* A_log, const float* D, float* ssm_state,
                              const int32_t* rows, bf16* g, int M, int d_inner, int dt_rank,
                              hipStream_t s);
-hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, bf16* out, int M,
-                               int d_model, int d_inner, hipStream_t s);
+// counters: zeroed by the launch_dec_in_proj of the same step (stream order).
+hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, int* counters,
+                               bf16* out, int M, int d_model, int d_inner, hipStream_t s);
 
 }  // namespace jm

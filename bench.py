@@ -197,8 +197,9 @@ def main():
           f"{ws.numel() / 2**30:.2f} GiB", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
-        a = torch.empty(2**30, dtype=torch.uint8, device=dev)
+        a = torch.ones(2**30, dtype=torch.uint8, device=dev)   # written first, so the copy reads HBM
         b = torch.empty_like(a)
+        torch.cuda.synchronize()
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b

@@ -4,8 +4,8 @@
 // (activations (tokens, K), nn.Linear-style weights (features, K)); they differ
 // only in the epilogue, which is a compile-time parameter (one kernel symbol per
 // projection). The bf16 path runs on gfx950 matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation); the fp32 path (small fp32
-// layers) is a plain LDS-tiled FMA kernel.
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation); the fp32 path runs on the fp32
+// matrix cores (v_mfma_f32_32x32x2f32, 64 x 64 tiles).
 //
 // Main bf16 kernel (K % 64 == 0):
 //   * 256 x 256 macro tile, 512 threads = 8 waves (two per SIMD, so one wave's
@@ -21,7 +21,8 @@
 //     slice's first fragments load while the current MFMAs run, and the instruction
 //     order is pinned with sched_group_barrier;
 //   * the MFMA "A" operand is the weight tile and "B" the activation tile, so a
-//     lane owns 4 consecutive output features of one token (8-byte bf16 stores);
+//     lane owns 4 consecutive output features of one token; tiles inside one output
+//     leave through a per-wave LDS area as whole 128-byte lines;
 //   * tile order: groups of 4 row blocks share a weight block, and each of the 8
 //     XCDs (workgroups are dealt to them round-robin) gets a contiguous range;
 //   * persistent: one workgroup per CU walks its tiles, issuing the next tile's first
@@ -579,45 +580,78 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
 }
 
 // ---- fp32 path ----------------------------------------------------------------------
-// 64x64 tile, 256 threads, each thread 4 tokens x 4 consecutive features.
-template <int BM, int BN, int BKF, int EPI>
+// fp32 layers on the fp32 matrix cores (v_mfma_f32_32x32x2f32: fp32 products and sums). 64 x 64
+// tile, 4 waves, wave w owns the 32 x 32 block of tokens 32 (w >> 1) and features 32 (w & 1);
+// as in the bf16 kernel the weight block is the "A" operand, so a lane ends up with 4 consecutive
+// features of one token. K goes through LDS in 16-deep slices (rows padded to 20 floats, so the
+// 16-byte row reads of 32 lanes spread over the banks); the next slice's global loads are in
+// flight while the current one is multiplied. One MFMA takes 2 values of K, one per half-wave;
+// each lane reads 4 consecutive K values of its row at once and feeds them to 4 MFMAs, the
+// values of a half-wave being K = 4h .. 4h+3 of each group of 8: the weight and token operands
+// use the same assignment, so every product W[n, k] X[m, k] is formed exactly once.
+constexpr int F32_BM = 64, F32_BN = 64, F32_BK = 16, F32_PITCH = 20;
+
+__device__ __forceinline__ float4 load_row4(const float* __restrict__ base, int64_t ld, int64_t row,
+                                            int64_t rows, int k, int K, bool vec_ok) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (row >= rows) return v;
+  const float* p = base + row * ld + k;
+  if (vec_ok && k + 4 <= K) return *reinterpret_cast<const float4*>(p);
+  if (k < K) v.x = p[0];
+  if (k + 1 < K) v.y = p[1];
+  if (k + 2 < K) v.z = p[2];
+  if (k + 3 < K) v.w = p[3];
+  return v;
+}
+
+template <int EPI>
 __global__ __launch_bounds__(256)
-void gemm_f32_kernel(const float* __restrict__ X, int64_t ldx,
-                     const float* __restrict__ W, int64_t ldw,
-                     int64_t M, int N, int K, EpiArgs epi) {
-  __shared__ float sX[BKF][BM + 4];
-  __shared__ float sW[BKF][BN + 4];
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
-  const int tid = threadIdx.x;
-  const int tx = tid % (BN / 4);   // feature group
-  const int ty = tid / (BN / 4);   // token group
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += BKF) {
-    for (int i = tid; i < BM * BKF; i += 256) {
-      int r = i / BKF, k = i % BKF;
-      int64_t row = m0 + r;
-      sX[k][r] = (row < M && k0 + k < K) ? X[row * ldx + k0 + k] : 0.0f;
-    }
-    for (int i = tid; i < BN * BKF; i += 256) {
-      int r = i / BKF, k = i % BKF;
-      int row = n0 + r;
-      sW[k][r] = (row < N && k0 + k < K) ? W[(int64_t)row * ldw + k0 + k] : 0.0f;
-    }
+void gemm_f32_mfma_kernel(const float* __restrict__ X, int64_t ldx,
+                          const float* __restrict__ W, int64_t ldw,
+                          int64_t M, int N, int K, EpiArgs epi) {
+  __shared__ __attribute__((aligned(16))) float sX[F32_BM * F32_PITCH];
+  __shared__ __attribute__((aligned(16))) float sW[F32_BN * F32_PITCH];
+  const int64_t m0 = (int64_t)blockIdx.y * F32_BM;
+  const int n0 = blockIdx.x * F32_BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = 32 * (wave >> 1), wn = 32 * (wave & 1);
+  const int half = lane >> 5, r32 = lane & 31;
+  // loader: thread t moves 4 consecutive K values of row t / 4 of each operand
+  const int lrow = tid >> 2, lcol = (tid & 3) * 4;
+  const bool xvec = (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+  const bool wvec = (ldw & 3) == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0;
+  float4 xv = load_row4(X, ldx, m0 + lrow, M, lcol, K, xvec);
+  float4 wv = load_row4(W, ldw, n0 + lrow, N, lcol, K, wvec);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  for (int k0 = 0; k0 < K; k0 += F32_BK) {
+    __syncthreads();   // every wave is done reading the previous slice
+    *reinterpret_cast<float4*>(&sX[lrow * F32_PITCH + lcol]) = xv;
+    *reinterpret_cast<float4*>(&sW[lrow * F32_PITCH + lcol]) = wv;
     __syncthreads();
-#pragma unroll 4
-    for (int k = 0; k < BKF; ++k) {
-      float xv[4], wv[4];
-      for (int i = 0; i < 4; ++i) xv[i] = sX[k][ty * 4 + i];
-      for (int j = 0; j < 4; ++j) wv[j] = sW[k][tx * 4 + j];
-      for (int i = 0; i < 4; ++i)
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+    if (k0 + F32_BK < K) {
+      xv = load_row4(X, ldx, m0 + lrow, M, k0 + F32_BK + lcol, K, xvec);
+      wv = load_row4(W, ldw, n0 + lrow, N, k0 + F32_BK + lcol, K, wvec);
     }
-    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < F32_BK / 8; ++g) {
+      const float4 a = *reinterpret_cast<const float4*>(&sW[(wn + r32) * F32_PITCH + 8 * g + 4 * half]);
+      const float4 b = *reinterpret_cast<const float4*>(&sX[(wm + r32) * F32_PITCH + 8 * g + 4 * half]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b.w, acc, 0, 0, 0);
+    }
   }
-  for (int i = 0; i < 4; ++i) {
-    int64_t m = m0 + ty * 4 + i;
-    if (m < M) epilogue<float, EPI>(epi, m, n0 + tx * 4, N, acc[i]);
+  // lane: token m0 + wm + lane % 32; registers 4q .. 4q+3: features n0 + wn + 8q + 4 half + 0..3
+  const int64_t m = m0 + wm + r32;
+  if (m < M) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      epilogue<float, EPI>(epi, m, n0 + wn + 8 * q + 4 * half, N, v);
+    }
   }
 }
 
@@ -926,12 +960,11 @@ hipError_t launch_bf16_epi(const bf16* X, int64_t ldx, const bf16* W, int64_t ld
 template <int EPI>
 hipError_t launch_f32_epi(const float* X, int64_t ldx, const float* W, int64_t ldw, int64_t M,
                           int N, int K, const EpiArgs& epi, hipStream_t s) {
-  constexpr int BM = 64, BN = 64, BKF = 16;
-  const int64_t gy = (M + BM - 1) / BM;
+  const int64_t gy = (M + F32_BM - 1) / F32_BM;
   if (gy > 65535) return hipErrorInvalidValue;
-  dim3 grid((N + BN - 1) / BN, (unsigned)gy);
-  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, BKF, EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw,
-                     M, N, K, epi);
+  dim3 grid((N + F32_BN - 1) / F32_BN, (unsigned)gy);
+  hipLaunchKernelGGL((gemm_f32_mfma_kernel<EPI>), grid, dim3(256), 0, s, X, ldx, W, ldw, M, N, K,
+                     epi);
   return hipGetLastError();
 }
 

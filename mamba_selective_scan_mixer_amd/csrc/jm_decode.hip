@@ -224,7 +224,8 @@ __global__ __launch_bounds__(256)
 void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W, int M, int N,
                          int K, int k_per_split, DecEpiArgs e) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // in scalar registers
   const int n0 = blockIdx.x * 64;
   const int split = blockIdx.y;
   const int kbeg = split * k_per_split;

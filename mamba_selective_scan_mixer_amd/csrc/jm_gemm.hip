@@ -292,6 +292,9 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
 
   const int n_tiles = tiles_m * tiles_n;
   const int lane = threadIdx.x & 63;
+  // The wave index stays a vector value here: taken through readfirstlane it makes the DMA
+  // address arithmetic scalar, but the compiler then waits on LDS twice more per K slice and
+  // spills scalar registers, and in_proj measured 8% slower.
   const int wave = threadIdx.x >> 6;
   const int wm0 = (wave / WAVES_N) * TM;
   const int wn0 = (wave % WAVES_N) * TN;
@@ -686,7 +689,7 @@ void dt_proj_softplus_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16
   constexpr int DPW = (NDMA + DT_NW - 1) / DT_NW;   // per wave (some idle when NDMA < DT_NW)
   __shared__ __attribute__((aligned(1024))) char sx[2][BLKB];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // in scalar registers
   const int kh = lane >> 5;
   const int ch = blockIdx.x * DT_CH + wave * 32 + (lane & 31);
   bf16x8 w[KS];
@@ -769,7 +772,7 @@ void xproj_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restric
   bf16* lds = reinterpret_cast<bf16*>(smem);
   const int64_t m0 = (int64_t)blockIdx.x * XP_BM;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // in scalar registers
   // DMA instructions (1 KB = 8 rows each): X 32 (4 per wave), W 36 (5 for waves 0-3, 4 after)
   constexpr int XI = 4, WI = 5;
   const int wi = wave < 4 ? 5 : 4;

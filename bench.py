@@ -83,14 +83,14 @@ def recorded_traffic(kernel: str):
         return None
 
 
-def recorded_valu(kernel: str):
-    """Measured wave-level VALU instructions per lane state update of a scan kernel, from the
-    committed rocprofv3 counter summary (SQ_INSTS_VALU x 64 / updates), or None when the scan
-    sources changed since the counters were taken."""
+def recorded_valu(kernel: str, profile: str = "prefill_128k_mfma_valu_counters.md",
+                  sources=("jm_scan.hip", "jm_internal.h")):
+    """Measured wave-level VALU instructions per lane state update of a scan kernel, from a
+    committed rocprofv3 counter summary (SQ_INSTS_VALU x 64 / updates), or None when the
+    kernel's sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "prefill_128k_mfma_valu_counters.md")
-    srcs = [os.path.join(ROOT, "mamba_selective_scan_mixer_amd", "csrc", f)
-            for f in ("jm_scan.hip", "jm_internal.h")]
+    path = os.path.join(ROOT, "profiles", profile)
+    srcs = [os.path.join(ROOT, "mamba_selective_scan_mixer_amd", "csrc", f) for f in sources]
     try:
         rec = None
         for line in open(path):
@@ -360,12 +360,24 @@ def run_scan_backward(jm, torch, wl, layer, dims, u, cu, T, steps: int = 3):
     # algorithmic bytes: inputs x_hat, z, dg (bf16), dt (fp32), B, C read once; dx, ddt, dz
     # (fp32) written once; dB, dC written once
     nbytes = T * di * (2 + 2 + 2 + 4 + 3 * 4) + T * 16 * 4 * 4
-    return {"ms_per_call": round(el * 1e3, 3), "tokens_per_s": round(T / el, 1), "steps": steps,
-            "algorithmic_bytes": nbytes,
-            "hbm_frac": round(nbytes / el / 1e9 / HBM_PEAK_GBS, 4),
-            "kernels_ms": {k: round(v[1] / max(v[0], 1), 4) for k, v in prof.items()},
-            "note": "gradients of the scan + D skip + gate step w.r.t. x_hat, Delta, B, C, z, "
-                    "A_log, D (fp32), 64-token chunks"}
+    kernels_ms = {k: round(v[1] / max(v[0], 1), 4) for k, v in prof.items()}
+    out = {"ms_per_call": round(el * 1e3, 3), "tokens_per_s": round(T / el, 1), "steps": steps,
+           "algorithmic_bytes": nbytes,
+           "hbm_frac": round(nbytes / el / 1e9 / HBM_PEAK_GBS, 4),
+           "kernels_ms": kernels_ms,
+           "note": "gradients of the scan + D skip + gate step w.r.t. x_hat, Delta, B, C, z, "
+                   "A_log, D (fp32), 64-token chunks; bound by VALU work, not HBM"}
+    # the main kernel against the VALU issue rate, with its measured instructions per update
+    per = recorded_valu("bwd_main", "scan_backward_128k_counters.md",
+                        ("jm_scan_bwd.hip", "jm_internal.h"))
+    if per is not None and kernels_ms.get("bwd_main"):
+        updates = T * di * 16
+        out["bwd_main"] = {"bound": "alu", "valu_per_update": per,
+                           "alu_frac": round(updates * per / VALU_LANE_OPS
+                                             / (kernels_ms["bwd_main"] * 1e-3), 4),
+                           "alu_basis": "measured VALU instructions per state update (rocprofv3 "
+                                        "SQ_INSTS_VALU, profiles/scan_backward_128k_counters.md)"}
+    return out
 
 
 def run_inner_norm(jm, torch, wl, dims, u, cu, out, fconv, fssm, ws, T, steps: int = 5):

@@ -40,6 +40,11 @@ CASES = {
     # dt_rank 128: the dt_proj kernel's 8-slice form (half its waves load no token rows)
     "rank128_bf16": ("prefill_4k", [150, 3, 203],
                      synth.LayerDims(d_model=512, d_inner=1024, d_state=16, d_conv=4, dt_rank=128)),
+    # fp32 matrix-core projections at odd widths: dt_proj K = 24 (one whole and one partial
+    # 16-deep slice), x_proj 56 outputs (less than one 64-wide tile), 3 / 5 / 10 feature tiles
+    # for out_proj / dt_proj / in_proj, 356 tokens (a ragged last 64-row tile)
+    "odd_fp32": ("tiny_fp32", [150, 3, 203],
+                 synth.LayerDims(d_model=192, d_inner=320, d_state=16, d_conv=4, dt_rank=24)),
 }
 
 

@@ -523,7 +523,10 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
                          "flushed), HIP events around the step",
             "algorithmic_bytes_per_step": per_step,
             "hbm_frac": per_step / (el / steps) / 1e9 / HBM_PEAK_GBS,
-            "kernels_us": {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in prof.items()}}
+            "kernels_us": {k: round(v[1] * 1e3 / max(v[0], 1), 2) for k, v in prof.items()},
+            "kernels_note": "eager steps with a HIP event pair around each launch (x_proj and "
+                            "out_proj include their split-K sums); the events add a few us per "
+                            "launch, so these sum to more than the graph-replayed step"}
 
 
 if __name__ == "__main__":

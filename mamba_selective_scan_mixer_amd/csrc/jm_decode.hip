@@ -151,10 +151,10 @@ __device__ __forceinline__ void dl_wait_vmcnt() {
 
 // out_proj's split-K epilogue. Each workgroup stores its 64 x 64 partial sums (16 per thread, as
 // 8-byte halves at [split][block][c][thread], so a wave's store covers 512 contiguous bytes) and
-// then counts itself in for its block of 64 features; the workgroup that arrives last reads the
-// other splits back and writes bf16(0 + p0 + p1 + p2 + p3), the sum of a separate reduction
-// launch in the same order. The workgroups of a block run on different XCDs, whose L2 caches are
-// not coherent with each other: the partial sums go through agent-scope atomic stores and loads,
+// then counts itself in for its block of 64 features; the workgroup that arrives last reads all
+// four partial sets back and writes bf16(0 + p0 + p1 + p2 + p3), the sum of a separate reduction
+// launch in the same order. The workgroups of a block may run on different XCDs, whose L2 caches
+// are not coherent with each other: the partial sums go through agent-scope atomic stores and loads,
 // which reach the device-coherent level, and only the ordering is fenced (every store has
 // completed, vmcnt(0), before the count moves; the reads start after the count is seen), so no
 // L2 write-back or invalidation is needed.

@@ -125,20 +125,12 @@ __device__ __forceinline__ void st1_at(float* row, uint32_t lo, float a) {
 #endif
 }
 
-// 4 / 2 consecutive activations as fp32 (bf16: the bit pattern shifted into the high half).
+// 4 consecutive activations as fp32 (bf16: the bit pattern shifted into the high half).
 __device__ __forceinline__ void load4f(const float* p, float v[4]) { load4(p, v); }
 __device__ __forceinline__ void load4f(const bf16* p, float v[4]) {
   const uint2 r = *reinterpret_cast<const uint2*>(p);
   v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
   v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xffff0000u);
-}
-__device__ __forceinline__ void load2f(const float* p, float v[2]) {
-  const float2 f = *reinterpret_cast<const float2*>(p);
-  v[0] = f.x; v[1] = f.y;
-}
-__device__ __forceinline__ void load2f(const bf16* p, float v[2]) {
-  const uint32_t r = *reinterpret_cast<const uint32_t*>(p);
-  v[0] = __uint_as_float(r << 16); v[1] = __uint_as_float(r & 0xffff0000u);
 }
 
 // Lane exchange through DPP (the add folds into v_add_f32_dpp).

@@ -451,10 +451,13 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
           __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
         } else {
           // half the MFMAs, the stage barrier, then the X DMA of stage kt+2 and the next
-          // stage's first fragments under the other half
+          // stage's first fragments under the other half. The wait before the barrier also
+          // covers this wave's fragment reads from the buffer the DMA after it refills (the
+          // scheduler may leave the last of them in flight there), so no wave's read can race
+          // another wave's DMA write (measured cost: 0.7% on in_proj).
           mfma_range(cur, 0, NM / 2);
           __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
-          wait_vmcnt<0>();
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
           issue_x(kt + 2, rb);
           load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);

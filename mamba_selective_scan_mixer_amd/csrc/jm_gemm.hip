@@ -487,7 +487,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
         if (s + 1 < SPS) {
           load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
         } else if (kt + 1 < nk) {
-          wait_vmcnt<0>();
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
           load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
         }
@@ -857,7 +857,11 @@ void xproj_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restric
         for (int b = 0; b < 4; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[a], fx[b], acc[a][b], 0, 0, 0);
     }
-    __builtin_amdgcn_s_barrier();      // every wave is done with this buffer
+    // Every wave is done with this buffer: its own reads have returned (the compiler may
+    // otherwise leave the last ones in flight and wait for them after the barrier, where
+    // another wave may already be refilling the buffer), then the barrier.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
   }
 
   // D block (16 features x 16 tokens): lane holds token lr, features 4 kg .. 4 kg + 3.

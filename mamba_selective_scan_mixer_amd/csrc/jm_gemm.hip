@@ -8,18 +8,22 @@
 // matrix cores (v_mfma_f32_32x32x2f32, 64 x 64 tiles).
 //
 // Main bf16 kernel (K % 64 == 0):
-//   * 256 x 256 macro tile, 512 threads = 8 waves (two per SIMD, so one wave's
-//     waits and address arithmetic overlap the other's MFMAs), wave tile 64 x 128;
+//   * 256 x 256 macro tile, 256 threads = 4 waves (one per SIMD), wave tile 128 x 128:
+//     16 accumulator blocks of 32 x 32 in AGPRs, a third less LDS fragment traffic per
+//     MFMA than 8 waves of 64 x 128 (the board runs at its power limit under these
+//     kernels, and the lower traffic buys clock);
 //   * operands go global -> LDS directly (buffer_load_dwordx4 ... lds, no VGPR
 //     staging) in 64-deep K slices (128-byte row segments) through two 64 KB
-//     buffers; each half of a slice's load is issued as soon as its buffer is free,
-//     and the waits are explicit vmcnt counts;
+//     buffers, and the waits are explicit vmcnt counts;
 //   * LDS rows are 64 bf16 = 8 chunks of 16 bytes; chunk c of row r sits at
 //     c ^ ((r & 7) ^ ((r >> 3) & 1)), which keeps the 16-byte fragment reads of 16
 //     consecutive rows on distinct banks (measured: no conflicts);
-//   * the barrier of each slice sits in the middle of its last k16 step: the next
-//     slice's first fragments load while the current MFMAs run, and the instruction
-//     order is pinned with sched_group_barrier;
+//   * with one wave per SIMD every stall of the wave idles its matrix core, so each k16
+//     step is issued in a fixed order (sched_barrier fences around each MFMA): MFMA q,
+//     then fragment read q of the next step, and after every second MFMA one of the 16
+//     DMA instructions of a later slice, spread so the address unit never backs up into
+//     the wave's instruction stream; the barrier of each slice sits in the middle of its
+//     last k16 step;
 //   * the MFMA "A" operand is the weight tile and "B" the activation tile, so a
 //     lane owns 4 consecutive output features of one token; tiles inside one output
 //     leave through a per-wave LDS area as whole 128-byte lines;
@@ -260,17 +264,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CNT) : "memory");
 }
 
-// 256 x 256 tiles, 8 waves, K slices of 64 (128-byte row segments: one L2 request per row per
+// 256 x 256 tiles, 4 waves, K slices of 64 (128-byte row segments: one L2 request per row per
 // slice, half the requests of 64-byte segments), two LDS buffers of 64 KB, and 4 KB per wave
 // behind them where the epilogue turns result rows into whole 128-byte lines.
-constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 4, MS_WN = 2, MS_BK = 64;
+constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 2, MS_WN = 2, MS_BK = 64;
+constexpr int MS_DMA_SPACING = 2;   // MFMAs between two DMA instructions of a wave
 constexpr int MS_EPI_WAVE_BYTES = 32 * 128;   // 32 token rows x 64 bf16 features
 constexpr int MS_LDS_BYTES =
     2 * (MS_BM + MS_BN) * MS_BK * 2 + MS_WM * MS_WN * MS_EPI_WAVE_BYTES;
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BKC, int EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __restrict__ W,
                       int64_t ldw, int64_t M, int N, int K, int tiles_m, int tiles_n,
                       EpiArgs epi) {
@@ -285,17 +290,18 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   constexpr int STAGE = (BM + BN) * BKC;     // bf16 elements per stage
   constexpr int NM = FN * FM;                // MFMAs per k16 step
   constexpr int NR = FN + FM;                // fragment reads per k16 step
-  static_assert(BKC == 64 && SPS == 4 && XI >= 1 && WI >= 1 && NM % 2 == 0, "tiling");
+  static_assert(BKC == 64 && SPS == 4 && XI == 8 && WI == 8 && NM == 16 && NR == 8,
+                "the issue order below is laid out for 4 waves of 128 x 128");
   static_assert(FN % 2 == 0, "the staged epilogue writes 64-feature row segments");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   bf16* lds = reinterpret_cast<bf16*>(smem);
 
   const int n_tiles = tiles_m * tiles_n;
   const int lane = threadIdx.x & 63;
-  // The wave index stays a vector value here: taken through readfirstlane it makes the DMA
-  // address arithmetic scalar, but the compiler then waits on LDS twice more per K slice and
-  // spills scalar registers, and in_proj measured 8% slower.
-  const int wave = threadIdx.x >> 6;
+  // The wave index in scalar registers: each DMA's LDS address (M0) is then scalar
+  // arithmetic; as a vector value every DMA needed a readfirstlane -> M0 chain that stalled
+  // the single wave of its SIMD (in_proj 14.7 -> 13.7 ms at 128K tokens).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm0 = (wave / WAVES_N) * TM;
   const int wn0 = (wave % WAVES_N) * TN;
   // this wave's epilogue staging area, behind the two stage buffers
@@ -391,9 +397,41 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
     }
   };
 
+  // Single-instruction pieces of the issue order. DMA j of a stage (j < XI: X rows, else W
+  // rows) fills 1 KB; fragment idx of a step (idx < FN: W, else X) is one 16-byte read.
+  auto dma1 = [&](int kt, int buf, int j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    char* base = reinterpret_cast<char*>(lds + buf * STAGE);
+    if (j < XI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void*)(base + (wave * XI + j) * 1024), 16,
+                                               xoff[j], kt * BKC * 2, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (lds_void*)(base + BM * BKC * 2 + (wave * WI + (j - XI)) * 1024), 16, woff[j - XI],
+          kt * BKC * 2, 0, 0);
+#endif
+  };
+  auto frag1 = [&](int buf, int s, int idx, int set) {
+    const int c = ((2 * s + khalf) ^ sw) << 3;
+    const bf16* st = lds + buf * STAGE;
+    if (idx < FN) fw[set][idx] = *reinterpret_cast<const bf16x8*>(&st[offW[idx] + c]);
+    else fx[set][idx - FN] = *reinterpret_cast<const bf16x8*>(&st[offX[idx - FN] + c]);
+  };
+  auto mf1 = [&](int cur, int i) {
+    const int a = i / FM, b = i % FM;
+    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[cur][a], fx[cur][b], acc[a][b], 0, 0, 0);
+  };
+  // a step's fragment reads in the order its MFMAs first use them: W0, X0..X3, W1..W3
+  constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+  constexpr int DSP = MS_DMA_SPACING;
+  // DMA j of stage kt+2 goes out at MFMA position DSP * j counted from the barrier in stage
+  // kt's last step; the first J0 of them fall in that step's second half, the rest into the
+  // first steps of stage kt+1.
+  constexpr int J0 = (NM / 2 + DSP - 1) / DSP;
+
   // Two buffers: stage kt lives in buffer kt & 1. The barrier that ends stage kt frees its
-  // buffer; the X half of stage kt+2 goes there at once, the W half during stage kt+1's first
-  // k16 step; both are waited for (vmcnt 0) before the barrier that ends stage kt+1.
+  // buffer for stage kt+2, whose 2 XI DMA instructions are spread over the following MFMAs as
+  // above; all are waited for (vmcnt 0) before the barrier that ends stage kt+1.
   const int nk = K / BKC;
   // store instructions this wave issues for a whole tile: the staged epilogue (1 KB of whole
   // lines each) and the per-element one (one per 4 results)
@@ -403,14 +441,18 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   setup(tile);
   issue_x(0, 0);
   issue_w(0, 0);
-  if (nk > 1) issue_x(1, 1);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < J0; ++j) dma1(1, 1, j);
+  }
   int stores_pending = 0;   // store instructions of the previous tile issued after these loads
   for (;;) {
     if (nk > 1) {
-      // stage 0 complete; stage 1's X half (and the previous tile's stores) may be in flight
-      if (stores_pending == NST) wait_vmcnt<XI + NST>();
-      else if (stores_pending == NST_LINES) wait_vmcnt<XI + NST_LINES>();
-      else wait_vmcnt<XI>();
+      // stage 0 complete; stage 1's first J0 DMAs (and the previous tile's stores) may be in
+      // flight (vmcnt counts to 63: beyond that the wait takes some of the stores too)
+      if (stores_pending == NST) wait_vmcnt<(J0 + NST > 63 ? 63 : J0 + NST)>();
+      else if (stores_pending == NST_LINES) wait_vmcnt<J0 + NST_LINES>();
+      else wait_vmcnt<J0>();
     } else {
       wait_vmcnt<0>();
     }
@@ -430,60 +472,52 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
 #pragma unroll
       for (int s = 0; s < SPS; ++s) {
         const int cur = s & 1;
-        if (s == 0) {
-          issue_w(kt + 1, rb ^ 1);
-          load_frags(rb, 1, fw[1], fx[1]);
-          mfma_range(0, 0, NM);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < SPS) {
+          // MFMA q, the next step's fragment read q, and stage kt+1's remaining DMAs
 #pragma unroll
           for (int q = 0; q < NM; ++q) {
-            if (q < WI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
-            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // 1 MFMA
+            __builtin_amdgcn_sched_barrier(0);
+            mf1(cur, q);
+            if (q < NR) frag1(rb, s + 1, kReadOrder[q], cur ^ 1);
+            const int pos = NM / 2 + NM * s + q;
+            if (pos % DSP == 0 && pos / DSP >= J0 && pos / DSP < XI + WI)
+              dma1(kt + 1, rb ^ 1, pos / DSP);
           }
-        } else if (s + 1 < SPS) {
-          load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
-          mfma_range(cur, 0, NM);
-#pragma unroll
-          for (int q = 0; q < NR; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
         } else {
-          // half the MFMAs, the stage barrier, then the X DMA of stage kt+2 and the next
-          // stage's first fragments under the other half. The wait before the barrier also
-          // covers this wave's fragment reads from the buffer the DMA after it refills (the
-          // scheduler may leave the last of them in flight there), so no wave's read can race
-          // another wave's DMA write (measured cost: 0.7% on in_proj).
-          mfma_range(cur, 0, NM / 2);
-          __builtin_amdgcn_sched_group_barrier(0x008, NM / 2, 0);
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-          __builtin_amdgcn_s_barrier();
-          issue_x(kt + 2, rb);
-          load_frags(rb ^ 1, 0, fw[cur ^ 1], fx[cur ^ 1]);
-          mfma_range(cur, NM / 2, NM);
-          constexpr int DPS = (XI + NM / 2 - 1) / (NM / 2);   // DMAs per MFMA slot
-          constexpr int RPS = (NR + NM / 2 - 1) / (NM / 2);   // reads per MFMA slot
+          // half the MFMAs, the stage barrier, then the other half with the next stage's first
+          // fragments and stage kt+2's first DMAs. The wait before the barrier also covers
+          // this wave's fragment reads from the buffer those DMAs refill, so no wave's read
+          // can race another wave's DMA write.
 #pragma unroll
           for (int q = 0; q < NM / 2; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            mf1(cur, q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
 #pragma unroll
-            for (int z = 0; z < DPS; ++z)
-              if (q * DPS + z < XI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-#pragma unroll
-            for (int z = 0; z < RPS; ++z)
-              if (q * RPS + z < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          for (int q = NM / 2; q < NM; ++q) {
+            __builtin_amdgcn_sched_barrier(0);
+            mf1(cur, q);
+            frag1(rb ^ 1, 0, kReadOrder[q - NM / 2], cur ^ 1);
+            const int pos = q - NM / 2;
+            if (pos % DSP == 0) dma1(kt + 2, rb, pos / DSP);
           }
         }
       }
     }
-    // Last two stages (nothing more to load after stage kt+1's W half).
+    // Last two stages: stage kt+1's DMAs not issued yet go out at once.
     for (; kt < nk; ++kt) {
       const int rb = kt & 1;
 #pragma unroll
       for (int s = 0; s < SPS; ++s) {
         const int cur = s & 1;
-        if (s == 0 && kt + 1 < nk) issue_w(kt + 1, rb ^ 1);
+        if (s == 0 && kt + 1 < nk) {
+#pragma unroll
+          for (int j = J0; j < XI + WI; ++j) dma1(kt + 1, rb ^ 1, j);
+        }
         if (s + 1 < SPS) {
           load_frags(rb, s + 1, fw[cur ^ 1], fx[cur ^ 1]);
         } else if (kt + 1 < nk) {
@@ -506,7 +540,10 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
       setup(next);
       issue_x(0, 0);
       issue_w(0, 0);
-      if (nk > 1) issue_x(1, 1);
+      if (nk > 1) {
+#pragma unroll
+        for (int j = 0; j < J0; ++j) dma1(1, 1, j);
+      }
     }
     // Lane owns features n = base + 8q + 4*(lane/32) + 0..3 of token m = base + lane%32.
     // A tile whose 256 features lie inside one output (every tile of STORE; of SPLIT2 when the
@@ -532,6 +569,16 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
       }
     }
     if (tile_out && (reinterpret_cast<uintptr_t>(tile_out) & 15) != 0) tile_out = nullptr;
+    // The accumulators leave the AGPRs four at a time, right where they are used, through
+    // inline-asm reads: read by plain code, all 256 were copied to VGPRs at once and half of
+    // them spilled. The hazard recognizer does not look inside inline asm, so 24 wait states
+    // separate the tile's last MFMA from the first read (32x32x16 results need 18).
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    auto acc4 = [&](int a, int b, int q, float v[4]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[u]) : "a"(acc[a][b][4 * q + u]));
+    };
     if ((EPI == EPI_STORE || EPI == EPI_SPLIT2) && tile_out) {
 #pragma unroll
       for (int b = 0; b < FM; ++b)
@@ -541,9 +588,10 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
           for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const f32x16& c = acc[2 * ap + j][b];
-              const bf16 h[4] = {from_f32<bf16>(c[4 * q]), from_f32<bf16>(c[4 * q + 1]),
-                                 from_f32<bf16>(c[4 * q + 2]), from_f32<bf16>(c[4 * q + 3])};
+              float c[4];
+              acc4(2 * ap + j, b, q, c);
+              const bf16 h[4] = {from_f32<bf16>(c[0]), from_f32<bf16>(c[1]),
+                                 from_f32<bf16>(c[2]), from_f32<bf16>(c[3])};
               const int chunk = 4 * j + q;   // features 8 chunk .. 8 chunk + 7 of the 64
               *reinterpret_cast<uint2*>(stg + lrow * 128 + ((chunk ^ (lrow & 7)) << 4) +
                                         khalf * 8) = *reinterpret_cast<const uint2*>(h);
@@ -568,8 +616,8 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int n = en0 + wn0 + a * 32 + 8 * q + 4 * khalf;
-            float v[4] = {acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2],
-                          acc[a][b][4 * q + 3]};
+            float v[4];
+            acc4(a, b, q, v);
             epilogue<bf16, EPI>(epi, m, n, N, v);
           }
         }

@@ -22,8 +22,8 @@
 //     step is issued in a fixed order (sched_barrier fences around each MFMA): MFMA q,
 //     then fragment read q of the next step, and after every second MFMA one of the 16
 //     DMA instructions of a later slice, spread so the address unit never backs up into
-//     the wave's instruction stream; the barrier of each slice sits in the middle of its
-//     last k16 step;
+//     the wave's instruction stream; the barrier of each slice opens its last k16 step
+//     (measured against the middle of it and a quarter in: 0.4-0.6% faster);
 //   * the MFMA "A" operand is the weight tile and "B" the activation tile, so a
 //     lane owns 4 consecutive output features of one token; tiles inside one output
 //     leave through a per-wave LDS area as whole 128-byte lines;
@@ -269,6 +269,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 // behind them where the epilogue turns result rows into whole 128-byte lines.
 constexpr int MS_BM = 256, MS_BN = 256, MS_WM = 2, MS_WN = 2, MS_BK = 64;
 constexpr int MS_DMA_SPACING = 2;   // MFMAs between two DMA instructions of a wave
+constexpr int MS_BARRIER_AT = 0;    // MFMAs of a slice's last k16 step before its barrier
 constexpr int MS_EPI_WAVE_BYTES = 32 * 128;   // 32 token rows x 64 bf16 features
 constexpr int MS_LDS_BYTES =
     2 * (MS_BM + MS_BN) * MS_BK * 2 + MS_WM * MS_WN * MS_EPI_WAVE_BYTES;
@@ -424,10 +425,12 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // a step's fragment reads in the order its MFMAs first use them: W0, X0..X3, W1..W3
   constexpr int kReadOrder[8] = {0, 4, 5, 6, 7, 1, 2, 3};
   constexpr int DSP = MS_DMA_SPACING;
+  constexpr int BAR = MS_BARRIER_AT;
+  static_assert(NM - BAR >= NR, "the next stage's first fragment reads follow the barrier");
   // DMA j of stage kt+2 goes out at MFMA position DSP * j counted from the barrier in stage
-  // kt's last step; the first J0 of them fall in that step's second half, the rest into the
+  // kt's last step; the first J0 of them fall in the rest of that step, the others into the
   // first steps of stage kt+1.
-  constexpr int J0 = (NM / 2 + DSP - 1) / DSP;
+  constexpr int J0 = (NM - BAR + DSP - 1) / DSP;
 
   // Two buffers: stage kt lives in buffer kt & 1. The barrier that ends stage kt frees its
   // buffer for stage kt+2, whose 2 XI DMA instructions are spread over the following MFMAs as
@@ -480,17 +483,17 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
             __builtin_amdgcn_sched_barrier(0);
             mf1(cur, q);
             if (q < NR) frag1(rb, s + 1, kReadOrder[q], cur ^ 1);
-            const int pos = NM / 2 + NM * s + q;
+            const int pos = NM - BAR + NM * s + q;
             if (pos % DSP == 0 && pos / DSP >= J0 && pos / DSP < XI + WI)
               dma1(kt + 1, rb ^ 1, pos / DSP);
           }
         } else {
-          // half the MFMAs, the stage barrier, then the other half with the next stage's first
-          // fragments and stage kt+2's first DMAs. The wait before the barrier also covers
-          // this wave's fragment reads from the buffer those DMAs refill, so no wave's read
-          // can race another wave's DMA write.
+          // BAR MFMAs, the stage barrier, then the rest with the next stage's first fragments
+          // and stage kt+2's first DMAs. The wait before the barrier also covers this wave's
+          // fragment reads from the buffer those DMAs refill, so no wave's read can race
+          // another wave's DMA write.
 #pragma unroll
-          for (int q = 0; q < NM / 2; ++q) {
+          for (int q = 0; q < BAR; ++q) {
             __builtin_amdgcn_sched_barrier(0);
             mf1(cur, q);
           }
@@ -498,11 +501,11 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
           asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
 #pragma unroll
-          for (int q = NM / 2; q < NM; ++q) {
+          for (int q = BAR; q < NM; ++q) {
             __builtin_amdgcn_sched_barrier(0);
             mf1(cur, q);
-            frag1(rb ^ 1, 0, kReadOrder[q - NM / 2], cur ^ 1);
-            const int pos = q - NM / 2;
+            if (q - BAR < NR) frag1(rb ^ 1, 0, kReadOrder[q - BAR], cur ^ 1);
+            const int pos = q - BAR;
             if (pos % DSP == 0) dma1(kt + 2, rb, pos / DSP);
           }
         }

@@ -432,9 +432,10 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
   // first steps of stage kt+1.
   constexpr int J0 = (NM - BAR + DSP - 1) / DSP;
 
-  // Two buffers: stage kt lives in buffer kt & 1. The barrier that ends stage kt frees its
-  // buffer for stage kt+2, whose 2 XI DMA instructions are spread over the following MFMAs as
-  // above; all are waited for (vmcnt 0) before the barrier that ends stage kt+1.
+  // Two buffers: stage kt lives in buffer kt & 1. The barrier in stage kt's last k16 step
+  // (every fragment of stage kt is in registers by then) frees its buffer for stage kt+2,
+  // whose 2 XI DMA instructions are spread over the following MFMAs as above; all are waited
+  // for (vmcnt 0) before the barrier in stage kt+1's last step.
   const int nk = K / BKC;
   // store instructions this wave issues for a whole tile: the staged epilogue (1 KB of whole
   // lines each) and the per-element one (one per 4 results)

@@ -577,6 +577,7 @@ void gemm_bf16_kernel(const bf16* __restrict__ X, int64_t ldx, const bf16* __res
     // inline-asm reads: read by plain code, all 256 were copied to VGPRs at once and half of
     // them spilled. The hazard recognizer does not look inside inline asm, so 24 wait states
     // separate the tile's last MFMA from the first read (32x32x16 results need 18).
+    __builtin_amdgcn_sched_barrier(0);   // no MFMA is scheduled past the guard
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     auto acc4 = [&](int a, int b, int q, float v[4]) {
 #pragma unroll

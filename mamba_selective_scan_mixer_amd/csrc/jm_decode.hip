@@ -6,7 +6,7 @@
 // the kernels here are built for bandwidth:
 //   dec_gemm_lds  64 output features x 64 tokens per workgroup, optional split-K over a
 //                 second grid dimension (fp32 partials). Weight and token rows reach LDS
-//                 through direct-to-LDS loads of whole 128-byte row segments, 7 stages of
+//                 through direct-to-LDS loads of whole 128-byte row segments, 5 stages of
 //                 64 K columns in flight; each wave owns a 32 x 32 output tile.
 //   in_proj epilogue: the conv-state shift, the causal conv (kernel 4) and SiLU are
 //                 applied right there for the x half; the z half is stored.
@@ -130,8 +130,9 @@ __device__ __forceinline__ void dec_inproj_item(const DecEpiArgs& e, int m, int 
 // instruction fetching 8 whole 128-byte row segments: loads straight into the MFMA operand
 // layout touch 32 lines per instruction and 32 bytes of each, and counters showed the address
 // unit stalled on the L1 for most of such a kernel. Stages of 64 K columns (16 KB: 64 weight
-// rows and 64 token rows) rotate through 8 LDS buffers, 7 in flight while one is read; each
-// wave issues a quarter of every stage's loads. Wave w owns the 32 x 32 output tile of features
+// rows and 64 token rows) rotate through DL_NBUF LDS buffers (6 for the decode projections),
+// all but the one being read in flight; each wave issues a quarter of every stage's loads.
+// Wave w owns the 32 x 32 output tile of features
 // 32 (w & 1) and tokens 32 (w >> 1) over the whole K range, so no partial sums cross waves.
 constexpr int DL_BK = 64;                       // K columns per stage
 constexpr int DL_TILE = 64 * DL_BK * 2;         // bytes of one operand's stage tile (8 KB)
@@ -317,8 +318,8 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
   const int pre = nst < DL_NBUF - 1 ? nst : DL_NBUF - 1;
   for (int t = 0; t < pre; ++t) issue(t, t);
   int t = 0;
-  // Steady state: stages t .. t+6 in flight (4 loads each per wave); once stage t has landed for
-  // every wave (wait, barrier), buffer t-1 is free and stage t+7 goes there.
+  // Steady state: stages t .. t+DL_NBUF-2 in flight (4 loads each per wave); once stage t has
+  // landed for every wave (wait, barrier), buffer t-1 is free and stage t+DL_NBUF-1 goes there.
   for (; t + DL_NBUF - 1 < nst; ++t) {
     dl_wait_vmcnt<4 * (DL_NBUF - 2)>();
     __builtin_amdgcn_s_barrier();
@@ -598,6 +599,9 @@ hipError_t launch_dec_gemm_lds(const bf16* U, const bf16* W, int M, int N, int K
 }
 
 constexpr int XPROJ_SPLIT_K = 512;   // K per workgroup for x_proj (16 splits at d_inner 8192)
+// LDS stage buffers of the in_proj and out_proj launches (measured per step at batch 64: 6
+// buffers 65.3-65.6 us, 8 buffers 66.0-66.6 us on one box)
+constexpr int DL_NBUF_DECODE = 6;
 
 }  // namespace
 
@@ -623,7 +627,8 @@ hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_
   e.counters = counters;
   e.n_counters = decode_fast_counters(d_model);
   e.d_inner = d_inner;
-  return launch_dec_gemm_lds<DEC_INPROJ_CONV>(u, W_in, M, 2 * d_inner, d_model, 1, e, s);
+  return launch_dec_gemm_lds<DEC_INPROJ_CONV, DL_NBUF_DECODE>(u, W_in, M, 2 * d_inner, d_model, 1,
+                                                              e, s);
 }
 
 hipError_t launch_dec_x_proj(const bf16* xh, const bf16* W_x, float* partial, bf16* delta,
@@ -666,8 +671,8 @@ hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial,
   e.partial = partial;
   e.counters = counters;
   e.out = out;
-  return launch_dec_gemm_lds<DEC_PARTIAL_SUM>(g, W_out, M, d_model, d_inner, OUTPROJ_SPLITS, e,
-                                              s);
+  return launch_dec_gemm_lds<DEC_PARTIAL_SUM, DL_NBUF_DECODE>(g, W_out, M, d_model, d_inner,
+                                                              OUTPROJ_SPLITS, e, s);
 }
 
 }  // namespace jm

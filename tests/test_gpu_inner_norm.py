@@ -114,3 +114,24 @@ def test_inner_norm_x_proj_stage(name):
     print(f"x_proj+norm {wl.dtype}: {e}", flush=True)
     assert e["delta"] < (8e-3 if wl.dtype == "bf16" else 1e-5), e
     assert max(e["B"], e["C"]) < 1e-5, e
+
+
+@pytest.mark.parametrize("dtype,dt_rank", [("bf16", 8), ("bf16", 24), ("f32", 264)])
+def test_inner_norm_row_shapes(dtype, dt_rank):
+    """The norm kernel's other row layouts: one 16-byte vector per delta row (64 rows per
+    wave), three vectors padded to four lanes, and 66 vectors (more than one per lane, so
+    the row loops); 150 tokens leave a ragged last wave. Bounds as above."""
+    dims = synth.LayerDims(d_model=64, d_inner=128, dt_rank=dt_rank)
+    wl = synth.make_workload("tiny_fp32", inner_norm=True, lengths=[150], dims=dims, dtype=dtype)
+    layer = device_layer(wl)
+    w = oracle.as_f64(wl.weights)
+    st = oracle.prefill(w, wl.u, wl.cu_seqlens, intermediates=True)["stages"][0]
+    xh = np.asarray(st["x_hat"])
+    xh = (synth.round_bf16(xh) if dtype == "bf16" else xh.astype(np.float32)).astype(np.float64)
+    d, B, C = jm.jm_stage_x_proj(layer, to_dev(xh, dtype))
+    torch.cuda.synchronize()
+    dr, Br, Cr = oracle.inner_norm(w, *oracle.x_proj(xh, w["x_proj_w"], dt_rank, wl.dims.d_state))
+    e = dict(delta=rel_err(to_np(d), dr), B=rel_err(to_np(B), Br), C=rel_err(to_np(C), Cr))
+    print(f"x_proj+norm {dtype} dt_rank {dt_rank}: {e}", flush=True)
+    assert e["delta"] < (8e-3 if dtype == "bf16" else 1e-5), e
+    assert max(e["B"], e["C"]) < 1e-5, e

@@ -293,7 +293,9 @@ def main():
     if not args.no_decode:
         decode = run_decode(jm, torch, dev, layer, dims, wl, args.decode_steps)
         print(f"[bench] decode {decode['us_per_step']:.1f} us/step, "
-              f"{decode['tokens_per_s'] / 1e6:.3f} M tok/s", file=sys.stderr, flush=True)
+              f"{decode['tokens_per_s'] / 1e6:.3f} M tok/s (cold {decode['us_per_step_cold']:.1f}; "
+              f"tiled weights {decode['us_per_step_tiled']:.1f}, cold "
+              f"{decode['us_per_step_cold_tiled']:.1f})", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -472,6 +474,31 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
         e1.record()
         e1.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
+    # the same steps from the decode copies of in_proj_w / out_proj_w in 64 x 64 tiles
+    # (jm_tile_decode_weights; bit-identical results): graph replay and cold, as above
+    dec_layer.tile_for_decode()
+    tgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(tgraph):
+        for s in range(G):
+            jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
+    tgraph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        tgraph.replay()
+    torch.cuda.synchronize()
+    el_tiled = (time.perf_counter() - t0) * steps / (reps * G)
+    cold_tiled = []
+    for s in range(min(32, steps)):
+        _ = scrub.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        jm.jamba_mamba_decode_step(dec_layer, toks[s], conv, ssm, out=out, workspace=ws)
+        e1.record()
+        e1.synchronize()
+        cold_tiled.append(e0.elapsed_time(e1) * 1e3)
+    del tgraph
+    dec_layer.drop_decode_tiles()
     del scrub
     # state cache: the same 64 sequences scattered over a 256-slot cache (random slot map),
     # decoded in place through the slot-indexed entry point, 16-step graph replayed
@@ -517,6 +544,11 @@ def run_decode(jm, torch, dev, layer, dims, wl_prefill, steps: int):
             "us_per_step_eager": el_eager * 1e6 / steps,
             "us_per_step_cold": round(float(np.median(cold)), 2),
             "us_per_step_state_cache": round(el_slots * 1e6 / steps, 2),
+            "us_per_step_tiled": round(el_tiled * 1e6 / steps, 2),
+            "us_per_step_cold_tiled": round(float(np.median(cold_tiled)), 2),
+            "tiled_note": "decode copies of in_proj_w / out_proj_w in 64 x 64 tiles "
+                          "(jm_tile_decode_weights, +201 MB; same outputs bit for bit), graph "
+                          "replay and cold as above",
             "state_cache_note": "the 64 states in random slots of a 256-slot cache, slot-indexed "
                                 "in-place decode (jamba_mamba_decode_step_slots), graph replay",
             "cold_note": "median of 32 single steps, each after a 1 GiB read (Infinity Cache "

@@ -90,6 +90,15 @@ typedef struct {
     const float *B_norm_w;    /* (d_state) fp32 or NULL                                        */
     const float *C_norm_w;    /* (d_state) fp32 or NULL                                        */
     float        norm_eps;
+    /* Optional decode copies of in_proj_w and out_proj_w in 64 x 64 tiles, filled by
+     * jm_tile_decode_weights (same size and dtype as the matrices they copy); both set or
+     * both NULL. Only the single-token decode reads them (jamba_mamba_decode_step and its
+     * _slots and _noalloc forms), with results bit for bit equal to those from the row-major
+     * matrices; the prefill reads the row-major ones. Set, they are accepted only where the
+     * bf16 decode kernels apply (d_model % 256 == 0, d_inner % 1024 == 0, dt_rank 128 or
+     * 256), else JM_ERR_UNSUPPORTED. */
+    const void  *in_proj_w_tiles;
+    const void  *out_proj_w_tiles;
 } jm_layer_weights;
 
 /* Human-readable name of a status. Never NULL. */
@@ -152,6 +161,24 @@ jm_status jamba_mamba_decode_step(const jm_layer_dims *dims, const jm_layer_weig
                                   const void *u, int32_t batch, void *conv_state,
                                   float *ssm_state, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/*
+ * Fill the decode copies of the two large projections: in_proj_w_tiles from in_proj_w
+ * (2*d_inner x d_model) and out_proj_w_tiles from out_proj_w (d_model x d_inner). Tile
+ * (b, s) of an N x K matrix holds rows 64b .. 64b+63 and columns 64s .. 64s+63 as 64 rows of
+ * 64 consecutive values; tiles are stored in order of b, then s. At one token per sequence
+ * the decode step's cost is streaming these matrices (201 MB at the Jamba-7B-class sizes),
+ * and a tile is one contiguous 8 KB run instead of 64 row pieces of 128 bytes, which reads
+ * HBM faster when the weights are not cached (serving runs many layers between two steps
+ * of one). The copies cost as much memory again as the two matrices. Bf16 layers with
+ * d_model % 256 == 0, d_inner % 1024 == 0 and dt_rank 128 or 256 only (else
+ * JM_ERR_UNSUPPORTED); all four pointers device memory, 16-byte aligned, the outputs
+ * distinct from the inputs. Enqueued on `stream`; the copies must not change while a decode
+ * that reads them runs.
+ */
+jm_status jm_tile_decode_weights(const jm_layer_dims *dims, const void *in_proj_w,
+                                 const void *out_proj_w, void *in_proj_w_tiles,
+                                 void *out_proj_w_tiles, void *stream);
 
 /* Bytes of the fixed device-side scratch that jamba_mamba_decode_step_noalloc uses on each
  * GPU (32 MiB: a decode step at the Jamba-7B-class sizes needs about 4.2 MB plus 64 KB per

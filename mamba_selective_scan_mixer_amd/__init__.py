@@ -41,7 +41,8 @@ class LayerDims(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "in_proj_w", "conv_w", "conv_b", "x_proj_w", "dt_proj_w", "dt_proj_b", "A_log", "D",
-        "out_proj_w", "dt_norm_w", "B_norm_w", "C_norm_w")] + [("norm_eps", ctypes.c_float)]
+        "out_proj_w", "dt_norm_w", "B_norm_w", "C_norm_w")] + [("norm_eps", ctypes.c_float)] + [
+        (n, ctypes.c_void_p) for n in ("in_proj_w_tiles", "out_proj_w_tiles")]
 
 
 class ChunkSegment(ctypes.Structure):
@@ -125,6 +126,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.c_int32, _P, _P, _P]
         L.jamba_mamba_decode_step_slots.argtypes = [
             D, W, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+        L.jm_tile_decode_weights.argtypes = [D, _P, _P, _P, _P, _P]
         for name in ("jm_prefill_workspace_size", "jm_decode_workspace_size", "jamba_mamba_prefill",
                      "jamba_mamba_decode_step", "jm_prefill_plan", "jm_set_scan_chunk_len",
                      "jm_profile_enable", "jm_profile_reset", "jm_profile_read",
@@ -133,7 +135,7 @@ def lib() -> ctypes.CDLL:
                      "jm_stage_decode_update", "jamba_mamba_decode_step_noalloc",
                      "jm_prefill_slots_workspace_size", "jamba_mamba_prefill_slots",
                      "jamba_mamba_decode_step_slots", "jm_scan_backward_workspace_size",
-                     "jamba_mamba_scan_backward"):
+                     "jamba_mamba_scan_backward", "jm_tile_decode_weights"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -193,6 +195,27 @@ class MambaLayer:
         self.struct = LayerWeights(*[(self.tensors[k].data_ptr() if self.tensors[k] is not None
                                       else None) for k in self.WEIGHT_KEYS + self.NORM_KEYS],
                                    self.norm_eps if self.inner_norm else 0.0)
+        self.tiles = None   # decode copies of in_proj_w / out_proj_w (tile_for_decode)
+
+    def tile_for_decode(self, stream=None) -> "MambaLayer":
+        """Add the decode copies of in_proj_w and out_proj_w in 64 x 64 tiles
+        (jm_tile_decode_weights); decode steps then read those (same results, bit for bit)."""
+        s = torch.cuda.current_stream() if stream is None else stream
+        with torch.cuda.stream(s):
+            ti = torch.empty_like(self.tensors["in_proj_w"])
+            to = torch.empty_like(self.tensors["out_proj_w"])
+            _check(lib().jm_tile_decode_weights(
+                ctypes.byref(self.dims), _ptr(self.tensors["in_proj_w"]),
+                _ptr(self.tensors["out_proj_w"]), _ptr(ti), _ptr(to), s.cuda_stream))
+        self.tiles = (ti, to)
+        self.struct.in_proj_w_tiles, self.struct.out_proj_w_tiles = ti.data_ptr(), to.data_ptr()
+        return self
+
+    def drop_decode_tiles(self) -> "MambaLayer":
+        """Decode from the row-major matrices again (frees the tiled copies)."""
+        self.struct.in_proj_w_tiles = self.struct.out_proj_w_tiles = None
+        self.tiles = None
+        return self
 
     @classmethod
     def from_arrays(cls, dims: LayerDims, arrays: Dict[str, "object"], device="cuda") -> "MambaLayer":

@@ -136,6 +136,23 @@ jm_status check_weights(const jm_layer_weights* w) {
     if (!aligned16(w->dt_norm_w) || !aligned16(w->B_norm_w) || !aligned16(w->C_norm_w))
       return fail(JM_ERR_ALIGNMENT, "inner norm gains must be 16-byte aligned");
   }
+  if ((w->in_proj_w_tiles != nullptr) != (w->out_proj_w_tiles != nullptr))
+    return fail(JM_ERR_INVALID_ARG, "decode tiles: in_proj_w_tiles and out_proj_w_tiles must be "
+                "both set or both NULL");
+  if (w->in_proj_w_tiles && (!aligned16(w->in_proj_w_tiles) || !aligned16(w->out_proj_w_tiles)))
+    return fail(JM_ERR_ALIGNMENT, "decode tiles must be 16-byte aligned");
+  return JM_OK;
+}
+
+bool decode_tiles_apply(const jm_layer_dims& d) {
+  return d.act_dtype == JM_BF16 && decode_fast_path_ok(d.d_model, d.d_inner, d.dt_rank);
+}
+
+// Decode entry points: tiled weights only where the bf16 decode kernels run.
+jm_status check_decode_tiles(const jm_layer_dims* d, const jm_layer_weights* w) {
+  if (w->in_proj_w_tiles && !decode_tiles_apply(*d))
+    return fail(JM_ERR_UNSUPPORTED, "decode tiles are read by the bf16 decode kernels only "
+                "(d_model %% 256 == 0, d_inner %% 1024 == 0, dt_rank 128 or 256)");
   return JM_OK;
 }
 
@@ -420,7 +437,9 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
     if (decode_fast_path_ok(dm, di, R)) {
       float* partial = reinterpret_cast<float*>(ws + L.partial);
       int* counters = reinterpret_cast<int*>(ws + L.counters);
-      const bf16* Win = static_cast<const bf16*>(w.in_proj_w);
+      const bool tiled = w.in_proj_w_tiles != nullptr;
+      const bf16* Win = static_cast<const bf16*>(tiled ? w.in_proj_w_tiles : w.in_proj_w);
+      const bf16* Wout = static_cast<const bf16*>(tiled ? w.out_proj_w_tiles : w.out_proj_w);
       for (int32_t b0 = 0; b0 < b; b0 += 64) {
         const int M = b - b0 < 64 ? b - b0 : 64;
         const bf16* ut = u + (int64_t)b0 * dm;
@@ -430,7 +449,7 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
         float* st = rows ? ssm_state : ssm_state + (int64_t)b0 * di * 16;
         const int32_t* rt = rows ? rows + b0 : nullptr;
         bf16* ot = out + (int64_t)b0 * dm;
-        JM_LAUNCH("dec_in_proj", launch_dec_in_proj(ut, Win, static_cast<const bf16*>(w.conv_w),
+        JM_LAUNCH("dec_in_proj", launch_dec_in_proj(ut, Win, tiled, static_cast<const bf16*>(w.conv_w),
                                                     static_cast<const bf16*>(w.conv_b), ct, rt, xh,
                                                     z, counters, M, dm, di, stream));
         JM_LAUNCH("dec_x_proj", launch_dec_x_proj(xh, static_cast<const bf16*>(w.x_proj_w),
@@ -441,8 +460,8 @@ jm_status run_decode(const jm_layer_dims& d, const jm_layer_weights& w, const T*
                                                w.norm_eps, M, R, stream));
         jm_status su = step_decode_update<bf16>(d, w, xh, z, delta, Bm, Cm, M, st, rt, g, stream);
         if (su != JM_OK) return su;
-        JM_LAUNCH("dec_out_proj", launch_dec_out_proj(g, static_cast<const bf16*>(w.out_proj_w),
-                                                      partial, counters, ot, M, dm, di, stream));
+        JM_LAUNCH("dec_out_proj", launch_dec_out_proj(g, Wout, tiled, partial, counters, ot, M,
+                                                      dm, di, stream));
       }
       return ok();
     }
@@ -584,6 +603,7 @@ jm_status check_decode_args(const jm_layer_dims* dims, const jm_layer_weights* w
   jm_status st = check_dims(dims);
   if (st != JM_OK) return st;
   if ((st = check_weights(weights)) != JM_OK) return st;
+  if ((st = check_decode_tiles(dims, weights)) != JM_OK) return st;
   if (batch < 0) return fail(JM_ERR_INVALID_ARG, "negative batch");
   if (batch == 0) return JM_OK;
   if (!u || !conv_state || !ssm_state || !out)
@@ -810,6 +830,41 @@ jm_status jamba_mamba_decode_step_noalloc(const jm_layer_dims* dims,
                          static_cast<hipStream_t>(stream_ptr));
 }
 
+jm_status jm_tile_decode_weights(const jm_layer_dims* dims, const void* in_proj_w,
+                                 const void* out_proj_w, void* in_proj_w_tiles,
+                                 void* out_proj_w_tiles, void* stream_ptr) {
+  jm_status st = check_dims(dims);
+  if (st != JM_OK) return st;
+  if (!decode_tiles_apply(*dims))
+    return fail(JM_ERR_UNSUPPORTED, "decode tiles are read by the bf16 decode kernels only "
+                "(d_model %% 256 == 0, d_inner %% 1024 == 0, dt_rank 128 or 256)");
+  if (!in_proj_w || !out_proj_w || !in_proj_w_tiles || !out_proj_w_tiles)
+    return fail(JM_ERR_INVALID_ARG, "weights and tiles must not be NULL");
+  const void* ptrs[] = {in_proj_w, out_proj_w, in_proj_w_tiles, out_proj_w_tiles};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(JM_ERR_ALIGNMENT, "a tensor argument is not 16-byte aligned");
+  const int dm = dims->d_model, di = dims->d_inner;
+  const size_t in_bytes = (size_t)2 * di * dm * 2, out_bytes = (size_t)dm * di * 2;
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const char *pa = static_cast<const char*>(a), *pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+  };
+  if (overlap(in_proj_w_tiles, in_bytes, in_proj_w, in_bytes) ||
+      overlap(in_proj_w_tiles, in_bytes, out_proj_w, out_bytes) ||
+      overlap(out_proj_w_tiles, out_bytes, in_proj_w, in_bytes) ||
+      overlap(out_proj_w_tiles, out_bytes, out_proj_w, out_bytes) ||
+      overlap(in_proj_w_tiles, in_bytes, out_proj_w_tiles, out_bytes))
+    return fail(JM_ERR_INVALID_ARG, "tiles overlap each other or the weights");
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  JM_LAUNCH("tile_in_proj", launch_tile_weights(static_cast<const bf16*>(in_proj_w),
+                                                static_cast<bf16*>(in_proj_w_tiles), 2 * di, dm,
+                                                stream));
+  JM_LAUNCH("tile_out_proj", launch_tile_weights(static_cast<const bf16*>(out_proj_w),
+                                                 static_cast<bf16*>(out_proj_w_tiles), dm, di,
+                                                 stream));
+  return ok();
+}
+
 // ---- state-cache (slot) entry points -----------------------------------------------------
 jm_status jm_prefill_slots_workspace_size(const jm_layer_dims* dims, int32_t n_seqs,
                                           int64_t total_tokens, size_t* bytes) {
@@ -878,6 +933,7 @@ jm_status jamba_mamba_decode_step_slots(const jm_layer_dims* dims,
                                         void* stream_ptr) {
   jm_status st = check_dims(dims);
   if (st != JM_OK || (st = check_weights(weights)) != JM_OK) return st;
+  if ((st = check_decode_tiles(dims, weights)) != JM_OK) return st;
   if (batch < 0 || n_slots < 1) return fail(JM_ERR_INVALID_ARG, "negative batch or n_slots < 1");
   if (batch == 0) return ok();
   if ((st = check_ptrs({u, conv_cache, ssm_cache, out}, {workspace})) != JM_OK) return st;

@@ -41,6 +41,7 @@ struct DecEpiArgs {
   float* partial;        // PARTIAL: (splits, M, N) fp32; PARTIAL_SUM: per split, block, thread
   int* counters;         // INPROJ: zeroed (n_counters); PARTIAL_SUM: arrivals per 64-feature block
   int n_counters;
+  int w_tiled;           // INPROJ, PARTIAL_SUM: W in 64 x 64 tiles (see tile_weights_kernel)
 };
 
 // ---- write-out of one item: token m, features n .. n+7 (n % 8 == 0) ------------------------
@@ -257,6 +258,11 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
   // chunk that the swizzle puts there. Rows past N (weights) or M (tokens) repeat the last row;
   // their results are never stored. Buffer loads: a descriptor per operand, 32-bit lane offsets,
   // the K advance in the scalar offset.
+  // Tiled weights (N a multiple of 64): the block's tiles follow each other along K, 8 KB
+  // apiece, so a load instruction reads one contiguous KB and a stage one contiguous 8 KB
+  // instead of 64 rows x 128 bytes at the row stride; lanes land in the same LDS positions.
+  const bool tiled = EPI != DEC_PARTIAL && e.w_tiled;
+  const int wstage = tiled ? DL_TILE : DL_BK * 2;   // weight bytes between stages
   uint32_t woff[2], uoff[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -264,7 +270,8 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
     const int c = (lane & 7) ^ dl_swz(r);
     const int wr = n0 + r < N ? r : N - 1 - n0;
     const int ur = r < M ? r : M - 1;
-    woff[i] = (uint32_t)(((int64_t)wr * K + kbeg + c * 8) * 2);
+    woff[i] = tiled ? (uint32_t)((kbeg / DL_BK) * DL_TILE + r * (DL_BK * 2) + c * 16)
+                    : (uint32_t)(((int64_t)wr * K + kbeg + c * 8) * 2);
     uoff[i] = (uint32_t)(((int64_t)ur * K + kbeg + c * 8) * 2);
   }
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -279,7 +286,7 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_void_t*)(base + (2 * wave + i) * 1024), 16,
-                                               woff[i], t * DL_BK * 2, 0, 0);
+                                               woff[i], t * wstage, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(urs,
                                                (lds_void_t*)(base + DL_TILE + (2 * wave + i) * 1024),
                                                16, uoff[i], t * DL_BK * 2, 0, 0);
@@ -356,6 +363,24 @@ void dec_gemm_lds_kernel(const bf16* __restrict__ U, const bf16* __restrict__ W,
       dec_inproj_item(e, m, n, v, s3[it], w4[it], b8[it]);
     else
       dec_store_item<EPI>(e, m, n, N, M, split, v);
+  }
+}
+
+// Decode copy of a projection's weights in 64 x 64 tiles: tile (b, s) = rows 64b .. 64b+63,
+// columns 64s .. 64s+63 of W (N x K, row-major), stored as 64 rows of 64 values, tiles in order
+// of b, then s. A workgroup copies one tile: 512 chunks of 16 bytes, two per thread, read as
+// 128-byte row segments and written contiguously.
+__global__ __launch_bounds__(256)
+void tile_weights_kernel(const bf16* __restrict__ W, bf16* __restrict__ tiles, int K) {
+  const int kt = K / 64;
+  const int64_t tile = blockIdx.x;
+  const int64_t b = tile / kt, st = tile % kt;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int q = threadIdx.x + 256 * h;        // chunk q: row q / 8, columns 8 (q % 8) ..
+    const int r = q >> 3, c = (q & 7) * 8;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(W + (64 * b + r) * (int64_t)K + 64 * st + c);
+    *reinterpret_cast<bf16x8*>(tiles + tile * 4096 + r * 64 + c) = v;
   }
 }
 
@@ -617,11 +642,19 @@ size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int bat
   return xp > op ? xp : op;
 }
 
-hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
+hipError_t launch_tile_weights(const bf16* W, bf16* tiles, int N, int K, hipStream_t s) {
+  if (N <= 0 || K <= 0 || N % 64 || K % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tile_weights_kernel, dim3((unsigned)((int64_t)(N / 64) * (K / 64))),
+                     dim3(256), 0, s, W, tiles, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, bool w_tiled, const bf16* conv_w,
                               const bf16* conv_b, bf16* conv_state, const int32_t* rows,
                               bf16* xh, bf16* z, int* counters, int M, int d_model, int d_inner,
                               hipStream_t s) {
   DecEpiArgs e = {};
+  e.w_tiled = w_tiled;
   e.xh = xh; e.z = z; e.conv_state = conv_state; e.rows = rows; e.conv_w = conv_w;
   e.conv_b = conv_b;
   e.counters = counters;
@@ -665,9 +698,11 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
   return hipGetLastError();
 }
 
-hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, int* counters,
-                               bf16* out, int M, int d_model, int d_inner, hipStream_t s) {
+hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, bool w_tiled, float* partial,
+                               int* counters, bf16* out, int M, int d_model, int d_inner,
+                               hipStream_t s) {
   DecEpiArgs e = {};
+  e.w_tiled = w_tiled;
   e.partial = partial;
   e.counters = counters;
   e.out = out;

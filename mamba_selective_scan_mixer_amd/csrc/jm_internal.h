@@ -156,7 +156,11 @@ size_t decode_fast_partial_floats(int d_model, int d_inner, int dt_rank, int bat
 int decode_fast_counters(int d_model);
 // rows: state row (slot) of each token row, or NULL for row m = token row m. counters:
 // decode_fast_counters(d_model) ints that in_proj sets to zero for the out_proj that follows.
-hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, const bf16* conv_w,
+// Decode copy of W (N x K, N and K multiples of 64) in 64 x 64 tiles, tile (b, s) = rows
+// 64b.., columns 64s.., tiles ordered by b then s, each 64 rows of 64 values.
+hipError_t launch_tile_weights(const bf16* W, bf16* tiles, int N, int K, hipStream_t s);
+// W_in / W_out: row-major, or in the tiles above when w_tiled.
+hipError_t launch_dec_in_proj(const bf16* u, const bf16* W_in, bool w_tiled, const bf16* conv_w,
                               const bf16* conv_b, bf16* conv_state, const int32_t* rows,
                               bf16* xh, bf16* z, int* counters, int M, int d_model, int d_inner,
                               hipStream_t s);
@@ -168,7 +172,8 @@ hipError_t launch_dec_update(const bf16* xh, const bf16* z, const bf16* delta, c
                              const int32_t* rows, bf16* g, int M, int d_inner, int dt_rank,
                              hipStream_t s);
 // counters: zeroed by the launch_dec_in_proj of the same step (stream order).
-hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, float* partial, int* counters,
-                               bf16* out, int M, int d_model, int d_inner, hipStream_t s);
+hipError_t launch_dec_out_proj(const bf16* g, const bf16* W_out, bool w_tiled, float* partial,
+                               int* counters, bf16* out, int M, int d_model, int d_inner,
+                               hipStream_t s);
 
 }  // namespace jm

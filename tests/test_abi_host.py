@@ -189,6 +189,33 @@ def test_noalloc_decode_validation_paths(L):
                                              None, None, None) == S["JM_OK"]
 
 
+def test_decode_tiles_validation_paths(L):
+    """Tiled decode weights: jm_tile_decode_weights and the decode entry points reject
+    unsupported widths, half-set, misaligned or overlapping tiles before touching the GPU."""
+    f = _Fake()
+    d = dims()
+    S = {n: i for i, n in enumerate(jm._STATUS)}
+    tile = lambda dd, a, b, c, e: L.jm_tile_decode_weights(ctypes.byref(dd), a, b, c, e, None)  # noqa: E731
+    tiny = jm.make_dims(64, 128, 16, 4, 8, jm.torch.float32)
+    odd = jm.make_dims(4096, 8192, 16, 4, 64, jm.torch.bfloat16)   # dt_rank 64: generic decode
+    assert tile(tiny, f(), f(), f(), f()) == S["JM_ERR_UNSUPPORTED"]
+    assert tile(odd, f(), f(), f(), f()) == S["JM_ERR_UNSUPPORTED"]
+    assert tile(d, f(), f(), None, f()) == S["JM_ERR_INVALID_ARG"]
+    assert tile(d, f(), f(), f() + 8, f()) == S["JM_ERR_ALIGNMENT"]
+    a, b = f(), f() + 0x10000000
+    assert tile(d, a, b, a + 256, b + 2 * 0x10000000) == S["JM_ERR_INVALID_ARG"]   # tiles over W_in
+    assert tile(d, a, b, a + 0x20000000, a + 0x20000000 + 4096) == S["JM_ERR_INVALID_ARG"]
+    need = jm.decode_workspace_size(d, 4)
+    call = lambda dd, w: L.jamba_mamba_decode_step(  # noqa: E731
+        ctypes.byref(dd), ctypes.byref(w), f(), 4, f(), f(), f(), f(), need, None)
+    assert call(d, _weights(f, in_proj_w_tiles=f())) == S["JM_ERR_INVALID_ARG"]
+    assert call(d, _weights(f, in_proj_w_tiles=f(), out_proj_w_tiles=f() + 8)) == S["JM_ERR_ALIGNMENT"]
+    assert call(odd, _weights(f, in_proj_w_tiles=f(), out_proj_w_tiles=f())) == S["JM_ERR_UNSUPPORTED"]
+    assert L.jamba_mamba_decode_step_noalloc(
+        ctypes.byref(odd), ctypes.byref(_weights(f, in_proj_w_tiles=f(), out_proj_w_tiles=f())),
+        f(), 4, f(), f(), f(), None) == S["JM_ERR_UNSUPPORTED"]
+
+
 def test_stage_validation_paths(L):
     """Every stage entry point rejects bad arguments on the host (nothing is launched)."""
     f = _Fake()

@@ -212,7 +212,8 @@ class MambaLayer:
         return self
 
     def drop_decode_tiles(self) -> "MambaLayer":
-        """Decode from the row-major matrices again (frees the tiled copies)."""
+        """Decode from the row-major matrices again (frees the tiled copies). A HIP graph
+        captured while the tiles were set keeps their addresses: do not replay it afterwards."""
         self.struct.in_proj_w_tiles = self.struct.out_proj_w_tiles = None
         self.tiles = None
         return self

@@ -6,8 +6,9 @@
 // the kernels here are built for bandwidth:
 //   dec_gemm_lds  64 output features x 64 tokens per workgroup, optional split-K over a
 //                 second grid dimension (fp32 partials). Weight and token rows reach LDS
-//                 through direct-to-LDS loads of whole 128-byte row segments, 5 stages of
-//                 64 K columns in flight; each wave owns a 32 x 32 output tile.
+//                 through direct-to-LDS loads of whole 128-byte row segments (or contiguous
+//                 runs from 64 x 64-tiled weights), 3 stages of 64 K columns in flight
+//                 (7 for x_proj); each wave owns a 32 x 32 output tile.
 //   in_proj epilogue: the conv-state shift, the causal conv (kernel 4) and SiLU are
 //                 applied right there for the x half; the z half is stored.
 //   out_proj epilogue: the workgroup that completes a 64-feature block last adds the four
@@ -131,7 +132,7 @@ __device__ __forceinline__ void dec_inproj_item(const DecEpiArgs& e, int m, int 
 // instruction fetching 8 whole 128-byte row segments: loads straight into the MFMA operand
 // layout touch 32 lines per instruction and 32 bytes of each, and counters showed the address
 // unit stalled on the L1 for most of such a kernel. Stages of 64 K columns (16 KB: 64 weight
-// rows and 64 token rows) rotate through DL_NBUF LDS buffers (6 for the decode projections),
+// rows and 64 token rows) rotate through DL_NBUF LDS buffers (4 for the decode projections),
 // all but the one being read in flight; each wave issues a quarter of every stage's loads.
 // Wave w owns the 32 x 32 output tile of features
 // 32 (w & 1) and tokens 32 (w >> 1) over the whole K range, so no partial sums cross waves.
@@ -624,9 +625,10 @@ hipError_t launch_dec_gemm_lds(const bf16* U, const bf16* W, int M, int N, int K
 }
 
 constexpr int XPROJ_SPLIT_K = 512;   // K per workgroup for x_proj (16 splits at d_inner 8192)
-// LDS stage buffers of the in_proj and out_proj launches (measured per step at batch 64: 6
-// buffers 65.3-65.6 us, 8 buffers 66.0-66.6 us on one box)
-constexpr int DL_NBUF_DECODE = 6;
+// LDS stage buffers of the in_proj and out_proj launches (measured per step at batch 64 on one
+// box, alternating builds: 4 buffers 60.8-60.9 us, 6 buffers 61.1-61.4, 8 buffers 61.4-61.5;
+// from the tiled weights 60.2 / 60.7 / 61.0-61.1)
+constexpr int DL_NBUF_DECODE = 4;
 
 }  // namespace
 

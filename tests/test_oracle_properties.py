@@ -1,7 +1,9 @@
 """Property tests of the CPU oracle (hypothesis): random tiny layer widths, packed sequence
 lengths, initial states, D and the optional inner norm, each compared with the independent
 pure-Python brute force of test_oracle_pins (products of decays written out, plain loops for
-every projection, the conv and the gate). Examples are derandomized, so the suite is repeatable.
+every projection, the conv and the gate); and the backward oracle over random packings against
+fp64 autograd of a forward written in torch ops. Examples are derandomized, so the suite is
+repeatable.
 """
 import numpy as np
 from hypothesis import given, settings, strategies as st
@@ -97,3 +99,40 @@ def test_scan_matches_brute_force(T, di, N, seed, h0_scale):
     y, h = oracle.selective_scan(x, dt, A, B, C, D, h0)
     yb, hb = brute_scan(x, dt, A, B, C, D, h0)
     assert rel_err(y, yb) < 1e-11 and rel_err(h, hb) < 1e-11
+
+
+@SETTINGS
+@given(st.lists(st.integers(1, 8), min_size=1, max_size=3), st.integers(1, 4), st.integers(1, 5),
+       st.integers(0, 2**31 - 1), st.booleans())
+def test_backward_matches_autograd(lengths, di, N, seed, states):
+    """The backward oracle over packed sequences against fp64 autograd of a forward written in
+    torch ops (per sequence: the state restarts, the loss adds sum(R * g) and sum(R2 * h_last))."""
+    import torch
+    import oracle.scan_backward as sb
+    rng = np.random.default_rng(seed)
+    T = sum(lengths)
+    n = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    c = dict(x=rng.standard_normal((T, di)),
+             dt=np.exp(rng.uniform(np.log(0.02), np.log(0.8), (T, di))),
+             A_log=rng.standard_normal((di, N)) * 0.5, B=rng.standard_normal((T, N)),
+             C=rng.standard_normal((T, N)), D=rng.standard_normal(di), z=rng.standard_normal((T, di)),
+             h0=rng.standard_normal((n, di, N)) * 0.5 if states else np.zeros((n, di, N)))
+    R = rng.standard_normal((T, di))
+    R2 = rng.standard_normal((n, di, N)) if states else np.zeros((n, di, N))
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in c.items()}
+    A = -torch.exp(t["A_log"])
+    loss = torch.zeros((), dtype=torch.float64)
+    for i in range(n):
+        h = t["h0"][i]
+        for j in range(int(cu[i]), int(cu[i + 1])):
+            h = torch.exp(t["dt"][j][:, None] * A) * h + (t["dt"][j] * t["x"][j])[:, None] * t["B"][j][None, :]
+            y = (h * t["C"][j][None, :]).sum(1) + t["D"] * t["x"][j]
+            loss = loss + (torch.tensor(R[j]) * y * t["z"][j] * torch.sigmoid(t["z"][j])).sum()
+        loss = loss + (torch.tensor(R2[i]) * h).sum()
+    loss.backward()
+    g = sb.scan_gate_backward_packed(c["x"], c["dt"], c["A_log"], c["B"], c["C"], c["D"], c["z"], R,
+                                     cu, c["h0"] if states else None, R2 if states else None)
+    for k, gk in {"x": "dx", "dt": "ddt", "A_log": "dA_log", "B": "dB", "C": "dC", "D": "dD",
+                  "z": "dz", "h0": "dh0"}.items():
+        assert rel_err(g[gk], t[k].grad.numpy()) < 1e-11, (k, lengths, di, N)

@@ -8,6 +8,7 @@ import subprocess
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import mamba_selective_scan_mixer_amd as jm
 
@@ -343,6 +344,14 @@ def test_plan_matches_independent_chunking(lengths, chunk_override):
     assert sum(s["end"] - s["begin"] for s in segs) == cu[-1]
     assert sum(s["starts_seq"] for s in segs) == len(lengths)
     assert sum(s["ends_seq"] for s in segs) == len(lengths)
+
+
+@settings(max_examples=60, deadline=None, derandomize=True)
+@given(st.lists(st.integers(1, 3000), min_size=1, max_size=12), st.sampled_from([0, 1, 7, 64, 256, 1000]))
+def test_plan_property(lengths, chunk_override):
+    """Random packings and chunk lengths: the library's plan equals the independent chunking,
+    and the chunks tile the tokens exactly once."""
+    test_plan_matches_independent_chunking(lengths, chunk_override)
 
 
 def test_plan_rejects_bad_cu():

@@ -69,7 +69,8 @@ typedef struct {
     int32_t weight_dtype;  /* jm_dtype of in/x/dt/out projections and conv weights */
 } jm_layer_dims;
 
-/* Layer parameters; element type `weight_dtype` unless marked fp32. */
+/* Layer parameters; element type `weight_dtype` unless marked fp32. Zero-initialise the
+ * struct (e.g. `jm_layer_weights w = {0};`) so that the optional fields read NULL / 0. */
 typedef struct {
     const void  *in_proj_w;   /* (2*d_inner, d_model): rows [0, d_inner) give x, the rest z */
     const void  *conv_w;      /* (d_inner, d_conv): tap d_conv-1 multiplies the current token */

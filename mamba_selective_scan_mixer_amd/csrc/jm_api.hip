@@ -659,7 +659,12 @@ jm_status scratch_for_current_device(char** out) {
 
 extern "C" {
 
-const char* jm_status_string(jm_status s) {
+const char* jm_status_string(jm_status status) {
+  // A C caller may pass any int; read the argument's bits as an int (a value outside the
+  // enumerators is not a valid jm_status in C++).
+  static_assert(sizeof(jm_status) == sizeof(int), "jm_status is an int");
+  int s;
+  std::memcpy(&s, &status, sizeof s);
   switch (s) {
     case JM_OK: return "JM_OK";
     case JM_ERR_INVALID_ARG: return "JM_ERR_INVALID_ARG";
